@@ -1,0 +1,120 @@
+/*
+ * fa.h - C ABI of the gfx950 (MI355X) attention-forward library (libfa.so).
+ *
+ * The library computes, for every batch b, query head h and query row i,
+ *
+ *     s_ij   = scale * <q[b,h,i,:], k[b,kvh,j,:]>       for the visible keys j
+ *     o[b,h,i,:] = sum_j softmax_j(s_ij) * v[b,kvh,j,:]
+ *     lse[b,h,i] = ln sum_j exp(s_ij)
+ *
+ * with kvh = h / (Hq / Hkv) (grouped-query / multi-query heads). This is the
+ * fused attention forward described in "Build Triton-Ascend Fused Attention"
+ * (Goal, Workflow, Implementation Pattern) and "Write Triton Attention Kernel"
+ * (Required reasoning process, steps 1-9; Correctness requirements); the
+ * score/softmax/output definition is the three-line forward of the
+ * "FlashAttention on Ascend: Triton-Ascend CV pipeline" notes, section 1.
+ * Without the causal flag every key is visible; with it, key j is visible to
+ * query row i iff j <= i (zero-based positions, mask anchored at the top-left
+ * corner, as in step 5c of "Write Triton Attention Kernel").
+ *
+ * Numerics: scores, the running row maximum, the softmax denominator and the
+ * output accumulator are fp32; probabilities are rounded to the input dtype
+ * (round to nearest even) before the P.V product; O is rounded to the input
+ * dtype only at the final store; LSE is fp32 in natural-log units.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+/* Element types of Q, K, V and O (all four share one type). */
+#define FA_DTYPE_F16 0
+#define FA_DTYPE_BF16 1
+
+/* Return codes. 0 is success; every error is negative. A validation error is
+ * reported before any HIP call: nothing is enqueued and O/LSE are untouched. */
+#define FA_OK 0
+#define FA_ERR_NULL -1      /* a required pointer (q, k, v, o, lse, a stride array, out) is NULL */
+#define FA_ERR_DTYPE -2     /* dtype is not FA_DTYPE_F16 or FA_DTYPE_BF16 */
+#define FA_ERR_HEAD_DIM -3  /* D is not one of 16, 32, 64, 128, 256 */
+#define FA_ERR_GQA -4       /* Hkv < 1 or Hq is not a multiple of Hkv */
+#define FA_ERR_SHAPE -5     /* a size is < 1, or a size or an addressed extent overflows */
+#define FA_ERR_LAYOUT -6    /* a d-stride is not 1, or a base address or b/h/n stride is not 16-byte aligned */
+#define FA_ERR_SCALE -7     /* scale is not a finite number > 0 */
+#define FA_ERR_HIP -8       /* the kernel launch failed (hipGetLastError after the launch) */
+
+/*
+ * fa_fwd - enqueue one attention forward on `stream` and return.
+ *
+ * q   : device pointer, Q viewed as (B, Hq, Nq, D) with element strides q_stride
+ * k   : device pointer, K viewed as (B, Hkv, Nkv, D) with element strides k_stride
+ * v   : device pointer, V viewed as (B, Hkv, Nkv, D) with element strides v_stride
+ * o   : device pointer, output O viewed as (B, Hq, Nq, D) with element strides o_stride
+ * lse : device pointer, fp32 logsumexp, contiguous (B, Hq, Nq): lse[(b*Hq + h)*Nq + i]
+ * *_stride : host arrays of 4 int64 element strides ordered (batch, head, sequence, dim).
+ *       The dim stride must be 1; the other strides must be >= 0 and, like every
+ *       base pointer, multiples of 16 bytes (the kernel moves 16-byte vectors).
+ *       Otherwise strides are free (BSND storage viewed as BNSD is fine). Zero
+ *       strides (broadcast views) are allowed for Q, K and V, not for O over a
+ *       dimension of size > 1.
+ * scale : score scale, a finite float > 0 (typically 1/sqrt(D)).
+ * causal: 0 = every key visible; nonzero = top-left causal mask (key j visible to row i iff j <= i).
+ * dtype : FA_DTYPE_F16 or FA_DTYPE_BF16, the element type of q, k, v and o.
+ * stream: a hipStream_t (NULL = the default stream).
+ *
+ * Sizes: 1 <= B, Hq, Hkv, Nq, Nkv < 2^31; D in {16, 32, 64, 128, 256}; Hq % Hkv == 0.
+ * Nq and Nkv need not be multiples of any tile size, and Nq may differ from Nkv.
+ *
+ * Ownership: the caller owns every buffer; the library keeps no state, allocates
+ * nothing and never synchronises. O and LSE must not overlap Q, K or V or each other.
+ * Calls are thread-safe. The launch is asynchronous: errors in the running kernel
+ * surface at the caller's next synchronisation, launch errors as FA_ERR_HIP.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+           const int64_t q_stride[4], const int64_t k_stride[4],
+           const int64_t v_stride[4], const int64_t o_stride[4],
+           float scale, int causal, int dtype, void* stream);
+
+/* Launch plan of fa_fwd for a shape, computed on the host without any HIP call. */
+typedef struct fa_plan {
+  int64_t grid;          /* workgroups launched */
+  int32_t block_threads; /* threads per workgroup */
+  int32_t block_q;       /* query rows per workgroup tile */
+  int32_t block_kv;      /* key/value rows per inner-loop tile */
+  int32_t lds_bytes;     /* LDS per workgroup */
+  int64_t tile_pairs;    /* (query tile, key tile) pairs the kernel visits, summed over all workgroups */
+} fa_plan;
+
+/* Fill *out with the plan fa_fwd would use. Same validation codes as fa_fwd
+ * (pointer and layout checks aside). */
+int fa_fwd_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                int causal, int dtype, fa_plan* out);
+
+/*
+ * Number of (query tile, key tile) pairs of an Nq x Nkv score matrix cut into
+ * bq x bkv tiles that a forward visits: all of them without the mask; with the
+ * top-left causal mask, for each query tile only the key tiles up to the one
+ * holding its last visible key (the loop bound of "Write Triton Attention
+ * Kernel", step 9, and the lower-triangle count of the Ascend notes, section 8).
+ * Returns -1 on sizes < 1.
+ */
+int64_t fa_tile_pairs(int64_t Nq, int64_t Nkv, int64_t bq, int64_t bkv, int causal);
+
+/* Static description of a return code (never NULL). */
+const char* fa_strerror(int code);
+
+/* FA_ABI_VERSION of the loaded library. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,127 @@
+"""ctypes binding of libfa.so. Argument marshalling only; every step of the
+attention forward runs in the library's kernels."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+FA_DTYPE_F16 = 0
+FA_DTYPE_BF16 = 1
+_DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG_DIR, "libfa.so")
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"fa error {code}: {msg}")
+        self.code = code
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("grid", ctypes.c_int64), ("block_threads", ctypes.c_int32), ("block_q", ctypes.c_int32),
+                ("block_kv", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("tile_pairs", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libfa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or lib_path
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m scaled_dot_product_fa2_amd.build`")
+    lib = ctypes.CDLL(p)
+    i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p, f32, i32,
+                           i32, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd_plan.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(_Plan)]
+    lib.fa_fwd_plan.restype = i32
+    lib.fa_tile_pairs.argtypes = [i64, i64, i64, i64, i32]
+    lib.fa_tile_pairs.restype = i64
+    lib.fa_strerror.argtypes = [i32]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def fa_strerror(code: int) -> str:
+    return load_library().fa_strerror(code).decode()
+
+
+def fa_version() -> int:
+    return load_library().fa_version()
+
+
+def fa_tile_pairs(Nq: int, Nkv: int, bq: int, bkv: int, causal: bool) -> int:
+    return load_library().fa_tile_pairs(Nq, Nkv, bq, bkv, int(bool(causal)))
+
+
+def _check(code: int):
+    if code != 0:
+        raise FaError(code, fa_strerror(code))
+
+
+def fa_fwd_plan(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int, causal: bool, dtype) -> dict:
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    plan = _Plan()
+    _check(load_library().fa_fwd_plan(B, Hq, Hkv, Nq, Nkv, D, int(bool(causal)), dt, ctypes.byref(plan)))
+    return {f: getattr(plan, f) for f, _ in _Plan._fields_}
+
+
+def _strides(t: torch.Tensor):
+    return (ctypes.c_int64 * 4)(*t.stride())
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+           scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None
+           ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention forward on BNSD tensors: returns (o, lse).
+
+    q: (B, Hq, Nq, D); k, v: (B, Hkv, Nkv, D); fp16 or bf16 on one GPU; any strides with a unit
+    head-dim stride and 16-byte aligned rows. ``scale`` defaults to 1/sqrt(D). ``out`` (same shape
+    and dtype as q) and ``lse`` (contiguous float32 (B, Hq, Nq)) may be passed in; otherwise they are
+    allocated. The kernel is enqueued on ``stream`` (default: the current stream).
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D (B, H, N, D)")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nkv, _ = k.shape
+    if k.shape != (B, Hkv, Nkv, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, D), dtype=q.dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must match q in shape, dtype and device")
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, Hq, Nq) tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    code = load_library().fa_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(out),
+        float(scale), int(bool(causal)), _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return out, lse

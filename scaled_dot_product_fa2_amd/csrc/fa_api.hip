@@ -1,0 +1,208 @@
+// fa_api.hip - C ABI of the gfx950 attention forward: validation, launch plan,
+// dispatch over (dtype, head_dim, causal) instances. The declarations and the
+// contract of every entry point are in include/fa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "fa.h"
+#include "fa_fwd_kernel.h"
+#include "fa_layout.h"
+
+namespace {
+
+using fa::FwdParams;
+using fa::TileCfg;
+
+// Tile configuration per head dim. Registers: D <= 128 fits two waves per SIMD
+// (two workgroups per CU, 64 KiB of LDS each); D = 256 keeps one wave per SIMD
+// and 128 KiB of LDS per workgroup.
+template <int D>
+struct CfgFor;
+template <> struct CfgFor<16> { typedef TileCfg<16, 4, 1, 64, 2> type; };
+template <> struct CfgFor<32> { typedef TileCfg<32, 4, 1, 64, 2> type; };
+template <> struct CfgFor<64> { typedef TileCfg<64, 4, 1, 64, 2> type; };
+template <> struct CfgFor<128> { typedef TileCfg<128, 4, 1, 64, 2> type; };
+template <> struct CfgFor<256> { typedef TileCfg<256, 4, 1, 64, 1> type; };
+
+struct PlanInfo {
+  int threads, bq, bkv, lds;
+};
+
+template <int D>
+PlanInfo plan_info() {
+  typedef typename CfgFor<D>::type C;
+  return PlanInfo{C::THREADS, C::BQ, C::BKV, C::LDS_BYTES};
+}
+
+bool plan_for_d(int64_t D, PlanInfo* out) {
+  switch (D) {
+    case 16: *out = plan_info<16>(); return true;
+    case 32: *out = plan_info<32>(); return true;
+    case 64: *out = plan_info<64>(); return true;
+    case 128: *out = plan_info<128>(); return true;
+    case 256: *out = plan_info<256>(); return true;
+    default: return false;
+  }
+}
+
+constexpr int64_t kMaxDim = (int64_t)std::numeric_limits<int32_t>::max();
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r); }
+bool add_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_add_overflow(a, b, r); }
+
+// Largest element offset addressed through a (b, h, n, d) stride set; false on overflow.
+bool extent_ok(int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* st) {
+  int64_t acc = D - 1, t;
+  if (!mul_ok(B - 1, st[0], &t) || !add_ok(acc, t, &acc)) return false;
+  if (!mul_ok(H - 1, st[1], &t) || !add_ok(acc, t, &acc)) return false;
+  if (!mul_ok(N - 1, st[2], &t) || !add_ok(acc, t, &acc)) return false;
+  return mul_ok(acc + 1, 2, &t);
+}
+
+int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int dtype,
+                PlanInfo* pi, int64_t* n_qtiles, int64_t* grid) {
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!plan_for_d(D, pi)) return FA_ERR_HEAD_DIM;
+  if (B < 1 || Hq < 1 || Nq < 1 || Nkv < 1 || Hkv < 0) return FA_ERR_SHAPE;
+  if (B > kMaxDim || Hq > kMaxDim || Hkv > kMaxDim || Nq > kMaxDim || Nkv > kMaxDim) return FA_ERR_SHAPE;
+  if (Hkv < 1 || Hq % Hkv != 0) return FA_ERR_GQA;
+  *n_qtiles = (Nq + pi->bq - 1) / pi->bq;
+  int64_t g;
+  if (!mul_ok(B, Hq, &g) || !mul_ok(g, *n_qtiles, &g) || g > kMaxDim) return FA_ERR_SHAPE;
+  int64_t lse_n;
+  if (!mul_ok(B, Hq, &lse_n) || !mul_ok(lse_n, Nq, &lse_n) || !mul_ok(lse_n, 4, &lse_n)) return FA_ERR_SHAPE;
+  *grid = g;
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_strides(const int64_t* st, bool is_output, int64_t B, int64_t H, int64_t N) {
+  if (st[3] != 1) return FA_ERR_LAYOUT;
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0) return FA_ERR_LAYOUT;
+    if ((st[i] * 2) % 16 != 0) return FA_ERR_LAYOUT;
+  }
+  if (is_output) {
+    if ((B > 1 && st[0] == 0) || (H > 1 && st[1] == 0) || (N > 1 && st[2] == 0)) return FA_ERR_LAYOUT;
+  }
+  return FA_OK;
+}
+
+template <typename T, bool CAUSAL, int D>
+int launch(const FwdParams& p, int64_t grid, hipStream_t stream) {
+  typedef typename CfgFor<D>::type C;
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, CAUSAL, C>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <typename T, bool CAUSAL>
+int launch_d(int64_t D, const FwdParams& p, int64_t grid, hipStream_t stream) {
+  switch (D) {
+    case 16: return launch<T, CAUSAL, 16>(p, grid, stream);
+    case 32: return launch<T, CAUSAL, 32>(p, grid, stream);
+    case 64: return launch<T, CAUSAL, 64>(p, grid, stream);
+    case 128: return launch<T, CAUSAL, 128>(p, grid, stream);
+    case 256: return launch<T, CAUSAL, 256>(p, grid, stream);
+    default: return FA_ERR_HEAD_DIM;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_strerror(int code) {
+  switch (code) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_DTYPE: return "unsupported dtype (expected FA_DTYPE_F16 or FA_DTYPE_BF16)";
+    case FA_ERR_HEAD_DIM: return "unsupported head dim (expected 16, 32, 64, 128 or 256)";
+    case FA_ERR_GQA: return "query heads must be a positive multiple of key/value heads";
+    case FA_ERR_SHAPE: return "sizes must be >= 1 and < 2^31, and addressed extents must not overflow";
+    case FA_ERR_LAYOUT:
+      return "unsupported layout (head-dim stride must be 1; strides >= 0 and pointers 16-byte aligned; "
+             "no zero output strides)";
+    case FA_ERR_SCALE: return "scale must be a finite number > 0";
+    case FA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+int64_t fa_tile_pairs(int64_t Nq, int64_t Nkv, int64_t bq, int64_t bkv, int causal) {
+  if (Nq < 1 || Nkv < 1 || bq < 1 || bkv < 1) return -1;
+  const int64_t n_qt = (Nq + bq - 1) / bq;
+  int64_t total = 0;
+  for (int64_t t = 0; t < n_qt; ++t) total += fa::kv_tiles_for_qtile(t * bq, bq, Nkv, bkv, causal != 0);
+  return total;
+}
+
+int fa_fwd_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, int dtype,
+                fa_plan* out) {
+  if (!out) return FA_ERR_NULL;
+  PlanInfo pi;
+  int64_t n_qt = 0, grid = 0;
+  const int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, &pi, &n_qt, &grid);
+  if (rc != FA_OK) return rc;
+  out->grid = grid;
+  out->block_threads = pi.threads;
+  out->block_q = pi.bq;
+  out->block_kv = pi.bkv;
+  out->lds_bytes = pi.lds;
+  out->tile_pairs = fa_tile_pairs(Nq, Nkv, pi.bq, pi.bkv, causal) * B * Hq;
+  return FA_OK;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+           int64_t Nq, int64_t Nkv, int64_t D, const int64_t q_stride[4], const int64_t k_stride[4],
+           const int64_t v_stride[4], const int64_t o_stride[4], float scale, int causal, int dtype,
+           void* stream) {
+  if (!q || !k || !v || !o || !lse || !q_stride || !k_stride || !v_stride || !o_stride) return FA_ERR_NULL;
+  PlanInfo pi;
+  int64_t n_qt = 0, grid = 0;
+  int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, &pi, &n_qt, &grid);
+  if (rc != FA_OK) return rc;
+  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_SCALE;
+  if ((rc = check_strides(q_stride, false, B, Hq, Nq)) != FA_OK) return rc;
+  if ((rc = check_strides(k_stride, false, B, Hkv, Nkv)) != FA_OK) return rc;
+  if ((rc = check_strides(v_stride, false, B, Hkv, Nkv)) != FA_OK) return rc;
+  if ((rc = check_strides(o_stride, true, B, Hq, Nq)) != FA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_LAYOUT;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_LAYOUT;
+  if (!extent_ok(B, Hq, Nq, D, q_stride) || !extent_ok(B, Hkv, Nkv, D, k_stride) ||
+      !extent_ok(B, Hkv, Nkv, D, v_stride) || !extent_ok(B, Hq, Nq, D, o_stride))
+    return FA_ERR_SHAPE;
+
+  FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
+  p.k_sb = k_stride[0]; p.k_sh = k_stride[1]; p.k_sn = k_stride[2];
+  p.v_sb = v_stride[0]; p.v_sh = v_stride[1]; p.v_sn = v_stride[2];
+  p.o_sb = o_stride[0]; p.o_sh = o_stride[1]; p.o_sn = o_stride[2];
+  p.B = (int32_t)B;
+  p.Hq = (int32_t)Hq;
+  p.Hkv = (int32_t)Hkv;
+  p.Nq = (int32_t)Nq;
+  p.Nkv = (int32_t)Nkv;
+  p.group = (int32_t)(Hq / Hkv);
+  p.n_qtiles = (int32_t)n_qt;
+  // scores enter the base-2 softmax as s * scale * log2(e), one fp32 FMA per score
+  p.c = (float)((double)scale * 1.4426950408889634074);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool cz = causal != 0;
+  if (dtype == FA_DTYPE_BF16)
+    return cz ? launch_d<__bf16, true>(D, p, grid, s) : launch_d<__bf16, false>(D, p, grid, s);
+  return cz ? launch_d<_Float16, true>(D, p, grid, s) : launch_d<_Float16, false>(D, p, grid, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,352 @@
+// fa_fwd_kernel.h - gfx950 (CDNA4) fused attention forward.
+//
+// One workgroup owns one (batch, query head, query tile) and streams the key /
+// value tiles of its key/value head past the query tile, as in the tiled
+// forward of "Write Triton Attention Kernel" (Required reasoning process,
+// steps 1-9) and the Ascend notes, section 1: the Q tile stays on chip, scores
+// and probabilities never leave registers, and O and LSE are written once.
+//
+// MI355X mapping:
+//  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 MFMAs (fp32
+//    accumulate). Every lane then owns one query row: the running maximum,
+//    denominator and rescale factor are per-lane scalars, and a row reduction
+//    is an in-register reduction plus one swap between the two wave halves.
+//  * The output is accumulated transposed as well, O^T += V^T P^T. The
+//    probability operand is taken from the score accumulators without any
+//    data movement (the reduction order of keys is permuted identically on
+//    both operands), and V^T fragments come from ds_read_b64_tr_b16
+//    transposing reads of a row-major V tile.
+//  * Q, K and V tiles move HBM -> LDS with 16-byte direct-to-LDS loads
+//    (global_load_lds), K/V double-buffered so the next tile streams in while
+//    the current one is consumed. Q is staged through LDS once and then kept in
+//    VGPRs for the whole key loop.
+//  * Softmax runs in base 2 with scale*log2(e) folded into one FMA per score
+//    (Ascend notes, section 1). m, l and the accumulator are fp32; P is rounded
+//    to the input dtype before the P.V product (all three pages).
+//  * Causal tiles above the diagonal are never visited; only key tiles that
+//    cross a wave's rows are masked ("Build Triton-Ascend Fused Attention",
+//    Workflow step 5; "Write Triton Attention Kernel", step 9 and Performance
+//    requirements).
+//  * D = 256 keeps eight 32-row accumulator blocks per query block, i.e. the two
+//    D128 halves of the Ascend notes (sections 1 and 7) each as four blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_layout.h"
+
+namespace fa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// Element traits: MFMA and round-to-nearest-even conversions per input type.
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<__bf16> {
+  typedef bf16x8 vec8;
+  typedef bf16x4 vec4;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Elem<_Float16> {
+  typedef f16x8 vec8;
+  typedef f16x4 vec4;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_sh, q_sn;  // element strides; the head-dim stride is 1
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int32_t B, Hq, Hkv, Nq, Nkv;
+  int32_t group;     // Hq / Hkv
+  int32_t n_qtiles;  // ceil(Nq / BQ)
+  float c;           // scale * log2(e)
+};
+
+// Tile configuration: NW waves per workgroup, QB 32-row query blocks per wave,
+// BKV keys per inner-loop tile.
+template <int D_, int NW_, int QB_, int BKV_, int WAVES_PER_SIMD_>
+struct TileCfg {
+  static constexpr int D = D_;
+  static constexpr int NW = NW_;
+  static constexpr int QB = QB_;
+  static constexpr int BKV = BKV_;
+  static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int BQ = NW * QB * 32;
+  static constexpr int KV_TILE_BYTES = BKV * D * 2;
+  static constexpr int Q_TILE_BYTES = BQ * D * 2;
+  // two stages of K and of V; the Q staging area aliases them before the loop
+  static constexpr int KV_BYTES = 4 * KV_TILE_BYTES;
+  static constexpr int LDS_BYTES = KV_BYTES > Q_TILE_BYTES ? KV_BYTES : Q_TILE_BYTES;
+  static_assert((BKV * chunks_per_row<D>()) % 64 == 0, "a K/V tile must be whole 64-lane copies");
+  static_assert((BQ * chunks_per_row<D>()) % 64 == 0, "a Q tile must be whole 64-lane copies");
+  static_assert(BKV % 32 == 0 && D % 32 == 0 || D == 16, "tile shape");
+};
+
+__device__ __forceinline__ float wave_half_max(float x) {
+  // max of the value in lane l and lane l^32
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Copy `rows` rows (a multiple of 64/chunks_per_row) of a [rows x D] 16-bit tile from global
+// memory into swizzled LDS with direct-to-LDS 16-byte loads. Rows at or past `row_limit` are
+// clamped to the last valid row (their values are never used unmasked).
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_tile(lds_char_t* lds_tile, const char* gbase, int64_t row_stride_bytes,
+                                         int row0, int row_limit, int wave, int lane) {
+  constexpr int n_inst = ROWS * chunks_per_row<D>() / 64;
+  constexpr int per_wave = (n_inst + NW - 1) / NW;
+#pragma unroll
+  for (int t = 0; t < per_wave; ++t) {
+    const int i = wave + t * NW;
+    if (n_inst % NW != 0 && i >= n_inst) break;
+    const RowChunk rc = dma_source<D>(i, lane);
+    int r = row0 + rc.row;
+    r = r < row_limit ? r : row_limit - 1;
+    const char* src = gbase + (int64_t)r * row_stride_bytes + rc.chunk * 16;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(lds_tile + i * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ i32x4 lds_read16(const lds_char_t* p) { return *(const lds_i32x4_t*)p; }
+__device__ __forceinline__ i16x4 lds_read_tr(const lds_char_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+}
+
+template <typename T, bool CAUSAL, class Cfg>
+__global__ void __launch_bounds__(Cfg::THREADS)
+    __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
+    fa_fwd_kernel(const FwdParams p) {
+  constexpr int D = Cfg::D, NW = Cfg::NW, QB = Cfg::QB, BKV = Cfg::BKV, BQ = Cfg::BQ;
+  constexpr int NS = D / 16;     // 16-wide head-dim slices (QK^T reduction steps)
+  constexpr bool DPAD = D < 32;  // D = 16: one 32-row O^T block, half of it padding
+  constexpr int NDB = DPAD ? 1 : D / 32;  // 32-row head-dim blocks of O^T
+  constexpr int NKB = BKV / 32;  // 32-row key blocks of S^T
+  constexpr int NKS = BKV / 16;  // 16-wide key slices (P.V reduction steps)
+  typedef typename Elem<T>::vec8 vec8;
+
+  __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::LDS_BYTES];
+  lds_char_t* const smem = (lds_char_t*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+
+  // ---- work mapping: workgroup -> (batch, query head, query tile), longest causal tiles first
+  const int64_t n_wg = (int64_t)p.B * p.Hq * p.n_qtiles;
+  const int64_t work = xcd_remap((int64_t)blockIdx.x, n_wg);
+  int qt = (int)(work % p.n_qtiles);
+  const int64_t bh = work / p.n_qtiles;
+  const int h = (int)(bh % p.Hq);
+  const int b = (int)(bh / p.Hq);
+  if (CAUSAL) qt = p.n_qtiles - 1 - qt;
+  const int kvh = h / p.group;
+  const int q0 = qt * BQ;
+
+  const char* qbase = (const char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
+  const char* kbase = (const char*)p.k + ((int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh) * 2;
+  const char* vbase = (const char*)p.v + ((int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh) * 2;
+
+  // ---- Q tile: HBM -> LDS (coalesced 16-byte loads), then LDS -> VGPRs in MFMA B-operand layout
+  dma_tile<D, BQ, NW>(smem, qbase, p.q_sn * 2, q0, p.Nq, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  vec8 qf[QB][NS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wave * QB * 32 + qfrag_row(qb, lane);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      i32x4 raw = lds_read16(smem + tile_chunk_offset<D>(row, kfrag_chunk(s, lane)));
+      qf[qb][s] = __builtin_bit_cast(vec8, raw);
+    }
+  }
+  __syncthreads();  // the Q staging area is reused for K/V below
+
+  // LDS stages: K[0], K[1], V[0], V[1]
+  auto k_lds = [&](int stage) { return smem + stage * Cfg::KV_TILE_BYTES; };
+  auto v_lds = [&](int stage) { return smem + (2 + stage) * Cfg::KV_TILE_BYTES; };
+
+  const int n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
+
+  // per-lane softmax state for each query block: running max (log2 units, scaled), partial denominator
+  float m_run[QB], l_run[QB];
+  f32x16 acc[QB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x16{};
+  }
+  // first and last query row owned by this wave
+  const int wq_first = q0 + wave * QB * 32;
+  const int wq_last = wq_first + QB * 32 - 1;
+  const float c = p.c;
+
+  dma_tile<D, BKV, NW>(k_lds(0), kbase, p.k_sn * 2, 0, p.Nkv, wave, lane);
+  dma_tile<D, BKV, NW>(v_lds(0), vbase, p.v_sn * 2, 0, p.Nkv, wave, lane);
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int st = j & 1;
+    const int k0 = j * BKV;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 < n_tiles) {
+      dma_tile<D, BKV, NW>(k_lds(st ^ 1), kbase, p.k_sn * 2, k0 + BKV, p.Nkv, wave, lane);
+      dma_tile<D, BKV, NW>(v_lds(st ^ 1), vbase, p.v_sn * 2, k0 + BKV, p.Nkv, wave, lane);
+    }
+    // A causal tile wholly to the right of this wave's last row contributes nothing.
+    if (CAUSAL && k0 > wq_last) continue;
+    const bool need_mask = (k0 + BKV > p.Nkv) || (CAUSAL && k0 + BKV - 1 > wq_first);
+
+    // ---- S^T = K Q^T for this tile
+    f32x16 sc[QB][NKB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sc[qb][kb] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const vec8 kf = __builtin_bit_cast(
+            vec8, lds_read16(k_lds(st) + tile_chunk_offset<D>(kfrag_row(kb, lane), kfrag_chunk(s, lane))));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = Elem<T>::mfma(kf, qf[qb][s], sc[qb][kb]);
+      }
+    }
+
+    // ---- online softmax (base 2), per lane = per query row
+    vec8 pf[QB][NKS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = wq_first + qfrag_row(qb, lane);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kb + acc_row(r, lane);
+            const bool hidden = (key >= p.Nkv) || (CAUSAL && key > qrow);
+            sc[qb][kb][r] = hidden ? -INFINITY : sc[qb][kb][r];
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
+      mx = wave_half_max(mx);
+      const float m_new = fmaxf(m_run[qb], mx * c);
+      // m_new is -inf only if every key seen so far is hidden from this row; then keep 0 as the shift
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
+      m_run[qb] = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][kb][r], c, -m_use));
+          sc[qb][kb][r] = pv;
+          rs += pv;
+        }
+      l_run[qb] = l_run[qb] * alpha + rs;
+      // rescale the accumulator only when some row's maximum moved (alpha == 1 is exact otherwise)
+      if (!__all(alpha == 1.f)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        vec8 t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = (T)sc[qb][ks >> 1][pv_src_reg(ks, e)];
+        pf[qb][ks] = t;
+      }
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const lds_char_t* vt = v_lds(st);
+        // D = 16 fills only the first 16 rows of the 32-row block; the other lanes read a valid
+        // address and contribute zeros.
+        const int col = DPAD ? (vtr_col(db, lane) & 15) : vtr_col(db, lane);
+        i16x4 lo = lds_read_tr(vt + tile_quad_offset<D>(vtr_row(ks, 0, lane), col));
+        i16x4 hi = lds_read_tr(vt + tile_quad_offset<D>(vtr_row(ks, 1, lane), col));
+        if (DPAD && ((lane >> 4) & 1)) {
+          lo = i16x4{};
+          hi = i16x4{};
+        }
+        const vec8 vf = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = Elem<T>::mfma(vf, pf[qb][ks], acc[qb][db]);
+      }
+    }
+  }
+
+  // ---- epilogue: O = acc / l (rounded once to T), LSE = (m + log2 l) * ln 2
+  const float LN2 = 0.69314718055994530942f;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = wq_first + qfrag_row(qb, lane);
+    const float l_tot = wave_half_sum(l_run[qb]);
+    const float inv = 1.f / l_tot;
+    if (qrow < p.Nq) {
+      char* orow = (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn) * 2;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < (DPAD ? D / 8 : 4); ++g4) {
+          typename Elem<T>::vec4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (T)(acc[qb][db][4 * g4 + e] * inv);
+          const int col = 32 * db + acc_row(4 * g4, lane);
+          *(i32x2*)(orow + col * 2) = __builtin_bit_cast(i32x2, ov);
+        }
+      if (half == 0) {
+        p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] = (m_run[qb] + __log2f(l_tot)) * LN2;
+      }
+    }
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,157 @@
+// Host-side check of the kernel's index arithmetic (fa_layout.h), built with g++.
+//
+// It simulates, for one wave, the gfx950 data movement the kernel relies on --
+// the direct-to-LDS tile copy, the 16-byte fragment reads, the transposing
+// ds_read_b64_tr_b16 reads and the MFMA 32x32x16 operand/accumulator layouts --
+// using the lane semantics stated in fa_layout.h, and checks that every MFMA
+// operand element is the tensor element the math needs. Exit code 0 = pass.
+#include <cstdio>
+#include <cstdlib>
+#include <map>
+#include <set>
+#include <vector>
+
+#include "fa_layout.h"
+
+static int g_fail = 0;
+#define CHECK(cond, ...)                 \
+  do {                                   \
+    if (!(cond)) {                       \
+      if (g_fail < 20) {                 \
+        std::printf("FAIL: " __VA_ARGS__); \
+        std::printf("\n");               \
+      }                                  \
+      ++g_fail;                          \
+    }                                    \
+  } while (0)
+
+// An LDS tile image: for every 16-bit slot, the (row, col) of the tensor element stored there.
+struct Elt {
+  int row, col;
+};
+
+template <int D>
+std::vector<Elt> dma_image(int rows) {
+  const int cpr = fa::chunks_per_row<D>();
+  const int n_inst = rows * cpr / 64;
+  std::vector<Elt> lds(rows * D, Elt{-1, -1});
+  std::set<std::pair<int, int>> seen;
+  for (int inst = 0; inst < n_inst; ++inst)
+    for (int lane = 0; lane < 64; ++lane) {
+      fa::RowChunk rc = fa::dma_source<D>(inst, lane);
+      CHECK(rc.row >= 0 && rc.row < rows && rc.chunk >= 0 && rc.chunk < cpr, "dma source out of tile D=%d", D);
+      CHECK(seen.insert({rc.row, rc.chunk}).second, "dma copies a chunk twice D=%d", D);
+      const int byte = inst * 1024 + lane * 16;  // where global_load_lds puts this lane's 16 bytes
+      CHECK(byte == fa::tile_chunk_offset<D>(rc.row, rc.chunk), "dma slot != tile_chunk_offset D=%d", D);
+      for (int e = 0; e < 8; ++e) lds[byte / 2 + e] = Elt{rc.row, rc.chunk * 8 + e};
+    }
+  CHECK((int)seen.size() == rows * cpr, "dma misses chunks D=%d", D);
+  return lds;
+}
+
+template <int D>
+void check_d() {
+  const int BKV = 64;
+  std::vector<Elt> lds = dma_image<D>(BKV);
+  const int NS = D / 16;
+  // K fragment (A operand of S^T = K Q^T): lane l must hold K[32kb + l%32][16s + 8(l/32) + e]
+  for (int kb = 0; kb < BKV / 32; ++kb)
+    for (int s = 0; s < NS; ++s)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int byte = fa::tile_chunk_offset<D>(fa::kfrag_row(kb, lane), fa::kfrag_chunk(s, lane));
+        for (int e = 0; e < 8; ++e) {
+          const Elt x = lds[byte / 2 + e];
+          CHECK(x.row == 32 * kb + lane % 32 && x.col == 16 * s + 8 * (lane / 32) + e, "K frag D=%d", D);
+        }
+      }
+  // V^T fragment (A operand of O^T = V^T P^T) via two transposing reads; lane l must hold
+  // V[key(ks, l, e)][32db + l%32] for e = 0..7 (lanes with l%32 >= D hold padding).
+  const int NDB = D < 32 ? 1 : D / 32;
+  for (int db = 0; db < NDB; ++db)
+    for (int ks = 0; ks < BKV / 16; ++ks)
+      for (int half = 0; half < 2; ++half) {
+        int addr[64];
+        for (int lane = 0; lane < 64; ++lane) {
+          int col = fa::vtr_col(db, lane);
+          if (D < 32) col &= 15;
+          addr[lane] = fa::tile_quad_offset<D>(fa::vtr_row(ks, half, lane), col);
+          CHECK(addr[lane] % 8 == 0 && addr[lane] >= 0 && addr[lane] + 8 <= BKV * D * 2, "tr addr D=%d", D);
+        }
+        for (int lane = 0; lane < 64; ++lane) {
+          if (D < 32 && ((lane >> 4) & 1)) continue;  // padding lanes are zeroed by the kernel
+          for (int e = 0; e < 4; ++e) {
+            const int src = 16 * (lane / 16) + 4 * e + (lane % 16) / 4;
+            const Elt x = lds[addr[src] / 2 + (lane % 4)];
+            const int ee = 4 * half + e;
+            CHECK(x.row == fa::pv_key(ks, lane, ee) && x.col == 32 * db + lane % 32, "V^T frag D=%d", D);
+          }
+        }
+      }
+  // bank behaviour of a 16-byte read phase (16 consecutive lanes): no two lanes on the same
+  // 16-byte slot of a 256-byte line unless they read the same address
+  for (int s = 0; s < NS; ++s)
+    for (int ph = 0; ph < 4; ++ph) {
+      std::map<int, int> slot_addr;
+      for (int lane = 16 * ph; lane < 16 * ph + 16; ++lane) {
+        const int byte = fa::tile_chunk_offset<D>(fa::kfrag_row(0, lane), fa::kfrag_chunk(s, lane));
+        const int slot = (byte / 16) % 16;
+        auto it = slot_addr.find(slot);
+        CHECK(it == slot_addr.end() || it->second == byte || D < 64, "K read bank conflict D=%d", D);
+        slot_addr[slot] = byte;
+      }
+    }
+}
+
+int main() {
+  check_d<16>();
+  check_d<32>();
+  check_d<64>();
+  check_d<128>();
+  check_d<256>();
+  // P^T operand taken from the S^T accumulators: register pv_src_reg(ks, e) of key block ks/2
+  for (int ks = 0; ks < 4; ++ks)
+    for (int lane = 0; lane < 64; ++lane)
+      for (int e = 0; e < 8; ++e) {
+        const int key = 32 * (ks / 2) + fa::acc_row(fa::pv_src_reg(ks, e), lane);
+        CHECK(key == fa::pv_key(ks, lane, e), "P operand key");
+      }
+  // pv_key is a bijection of the 16 keys of a slice onto operand positions
+  for (int ks = 0; ks < 2; ++ks) {
+    std::set<int> keys;
+    for (int lane = 0; lane < 64; lane += 32)
+      for (int e = 0; e < 8; ++e) keys.insert(fa::pv_key(ks, lane, e));
+    CHECK((int)keys.size() == 16 && *keys.begin() == 16 * ks && *keys.rbegin() == 16 * ks + 15, "pv_key perm");
+  }
+  // the workgroup remap is a bijection
+  for (long n = 1; n < 300; ++n) {
+    std::vector<int> hit(n, 0);
+    for (long w = 0; w < n; ++w) {
+      long l = fa::xcd_remap(w, n);
+      CHECK(l >= 0 && l < n, "xcd_remap range n=%ld", n);
+      if (l >= 0 && l < n) hit[l]++;
+    }
+    for (long l = 0; l < n; ++l) CHECK(hit[l] == 1, "xcd_remap not bijective n=%ld", n);
+  }
+  // key tiles per query tile against a brute-force scan of the visible (row, key) pairs
+  for (int nq : {1, 7, 64, 100, 128, 300})
+    for (int nkv : {1, 5, 64, 130, 257})
+      for (int bq : {32, 128})
+        for (int bkv : {32, 64})
+          for (int causal = 0; causal < 2; ++causal)
+            for (int q0 = 0; q0 < nq; q0 += bq) {
+              int need = 0;
+              for (int i = q0; i < q0 + bq && i < nq; ++i)
+                for (int j = 0; j < nkv; ++j)
+                  if (!causal || j <= i) need = need > j / bkv + 1 ? need : j / bkv + 1;
+              const long got = fa::kv_tiles_for_qtile(q0, bq, nkv, bkv, causal);
+              // the kernel may visit a tile that only rows past nq would see (they are never stored)
+              CHECK(got >= need && got <= (nkv + bkv - 1) / bkv, "kv tiles nq=%d nkv=%d", nq, nkv);
+              if (q0 + bq <= nq) CHECK(got == need, "kv tiles exact nq=%d nkv=%d", nq, nkv);
+            }
+  if (g_fail) {
+    std::printf("%d layout checks failed\n", g_fail);
+    return 1;
+  }
+  std::printf("layout self-test passed\n");
+  return 0;
+}

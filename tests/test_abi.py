@@ -1,0 +1,140 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/fa.h declares, and
+rejects every invalid call before touching HIP. Only invalid calls are made here (validation
+returns before any HIP call), so nothing is ever launched."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+LIB = os.path.join(ROOT, "scaled_dot_product_fa2_amd", "libfa.so")
+
+
+def _lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libfa.so is not built (python -m scaled_dot_product_fa2_amd.build)")
+    from scaled_dot_product_fa2_amd import _binding
+    return _binding.load_library()
+
+
+def _header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\**\s+\**(fa_[a-z0-9_]+)\s*\(", src, re.M)))
+
+
+def _header_defines():
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(FA_[A-Z0-9_]+)\s+(-?\d+)", open(HEADER).read())}
+
+
+def test_exports_every_declared_function():
+    names = _header_functions()
+    assert set(names) >= {"fa_fwd", "fa_fwd_plan", "fa_tile_pairs", "fa_strerror", "fa_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\w+)$", out, re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    lib = _lib()
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_version_and_strerror():
+    lib = _lib()
+    d = _header_defines()
+    assert lib.fa_version() == d["FA_ABI_VERSION"]
+    codes = [v for k, v in d.items() if k.startswith("FA_ERR_") or k == "FA_OK"]
+    msgs = {lib.fa_strerror(c).decode() for c in codes}
+    assert len(msgs) == len(codes), "every code has its own message"
+    assert lib.fa_strerror(12345).decode() == "unknown error code"
+
+
+def _st(*s):
+    return (ctypes.c_int64 * 4)(*s)
+
+
+VALID = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=0x50000, B=1, Hq=2, Hkv=1, Nq=128, Nkv=128,
+             D=64, qs=(16384, 8192, 64, 1), ks=(8192, 8192, 64, 1), vs=(8192, 8192, 64, 1),
+             os=(16384, 8192, 64, 1), scale=0.125, causal=0, dtype=1)
+
+
+def _call(**over):
+    a = dict(VALID)
+    a.update(over)
+    lib = _lib()
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"],
+                      a["D"], _st(*a["qs"]) if a["qs"] else None, _st(*a["ks"]) if a["ks"] else None,
+                      _st(*a["vs"]) if a["vs"] else None, _st(*a["os"]) if a["os"] else None, a["scale"],
+                      a["causal"], a["dtype"], None)
+
+
+D_ = _header_defines()
+BAD = [
+    ("null_q", dict(q=0), "FA_ERR_NULL"), ("null_lse", dict(lse=0), "FA_ERR_NULL"),
+    ("null_stride", dict(ks=None), "FA_ERR_NULL"),
+    ("dtype", dict(dtype=7), "FA_ERR_DTYPE"),
+    ("head_dim_48", dict(D=48), "FA_ERR_HEAD_DIM"), ("head_dim_512", dict(D=512), "FA_ERR_HEAD_DIM"),
+    ("gqa_3_2", dict(Hq=3, Hkv=2), "FA_ERR_GQA"), ("gqa_hkv0", dict(Hkv=0), "FA_ERR_GQA"),
+    ("zero_nq", dict(Nq=0), "FA_ERR_SHAPE"), ("zero_nkv", dict(Nkv=0), "FA_ERR_SHAPE"),
+    ("neg_b", dict(B=-1), "FA_ERR_SHAPE"), ("huge_n", dict(Nq=1 << 31), "FA_ERR_SHAPE"),
+    ("huge_extent", dict(qs=(1 << 61, 8192, 64, 1), B=8), "FA_ERR_SHAPE"),
+    ("d_stride", dict(qs=(16384, 8192, 64, 2)), "FA_ERR_LAYOUT"),
+    ("odd_row_stride", dict(ks=(8192, 8192, 60, 1)), "FA_ERR_LAYOUT"),
+    ("neg_stride", dict(vs=(8192, -8192, 64, 1)), "FA_ERR_LAYOUT"),
+    ("zero_out_stride", dict(os=(16384, 0, 64, 1)), "FA_ERR_LAYOUT"),
+    ("misaligned_ptr", dict(k=0x20008), "FA_ERR_LAYOUT"), ("misaligned_lse", dict(lse=0x50002), "FA_ERR_LAYOUT"),
+    ("scale_zero", dict(scale=0.0), "FA_ERR_SCALE"), ("scale_neg", dict(scale=-0.1), "FA_ERR_SCALE"),
+    ("scale_nan", dict(scale=float("nan")), "FA_ERR_SCALE"), ("scale_inf", dict(scale=float("inf")), "FA_ERR_SCALE"),
+]
+
+
+@pytest.mark.parametrize("name,over,code", BAD, ids=[b[0] for b in BAD])
+def test_validation_rejects(name, over, code):
+    assert _call(**over) == D_[code]
+
+
+def test_plan_and_tile_pairs():
+    from scaled_dot_product_fa2_amd import fa_fwd_plan, fa_tile_pairs
+    p = fa_fwd_plan(4, 16, 16, 1024, 1024, 128, False, 1)
+    assert p["grid"] == 4 * 16 * ((1024 + p["block_q"] - 1) // p["block_q"])
+    assert p["block_threads"] % 64 == 0 and p["lds_bytes"] <= 160 * 1024
+    nq_t = 1024 // p["block_q"]
+    nkv_t = 1024 // p["block_kv"]
+    assert p["tile_pairs"] == 4 * 16 * nq_t * nkv_t
+    pc = fa_fwd_plan(4, 16, 16, 1024, 1024, 128, True, 1)
+    assert pc["tile_pairs"] < p["tile_pairs"]
+    assert fa_tile_pairs(0, 5, 4, 4, True) == -1
+
+
+def test_causal_tile_count_golden():
+    """The lower-triangle tile count printed for an 8 x 8 tile grid (tests/golden/causal_tiles.json)."""
+    from scaled_dot_product_fa2_amd import fa_tile_pairs
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "causal_tiles.json")))
+    for case in g["cases"]:
+        n = case["tiles_per_side"] * case["tile"]
+        assert fa_tile_pairs(n, n, case["tile"], case["tile"], False) == case["full_tiles"]
+        assert fa_tile_pairs(n, n, case["tile"], case["tile"], True) == case["causal_tiles"]
+        saved = 1 - case["causal_tiles"] / case["full_tiles"]
+        assert abs(saved - case["saved_fraction"]) < 1e-12
+
+
+def test_layout_selftest_cpp(tmp_path):
+    """The kernel's index arithmetic, simulated lane by lane on the CPU (tests/layout_selftest.cpp)."""
+    exe = tmp_path / "layout_selftest"
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", os.path.join(ROOT, "scaled_dot_product_fa2_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "layout_selftest.cpp"), "-o", str(exe)], check=True)
+    res = subprocess.run([str(exe)], stdout=subprocess.PIPE, text=True)
+    assert res.returncode == 0, res.stdout
+
+
+def test_product_path_has_no_cpu_fallback():
+    """The binding never imports the oracle and raises when the library is missing."""
+    src = open(os.path.join(ROOT, "scaled_dot_product_fa2_amd", "_binding.py")).read()
+    assert "oracle" not in src
+    from scaled_dot_product_fa2_amd import _binding
+    with pytest.raises(RuntimeError):
+        _binding.load_library("/nonexistent/libfa.so")
