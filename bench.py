@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 attention forward on one MI355X.
+
+One step is one forward of the workload without the mask followed by one with
+the causal mask (B=4, Hq=Hkv=16, Nq=Nkv=1024, D=128, bf16, scale 1/sqrt(128),
+seeded N(0,1) inputs already resident in HBM). FLOP per forward is
+4*B*Hq*Nq*Nkv*D, halved for the causal mask. `value` is total FLOP / total time.
+
+Prints ONE JSON line. Extra objects:
+  roofline      - the dominant launch (the non-causal forward): algorithmic FLOP / its average
+                  duration from HIP events on the launch stream, against the dense bf16 MFMA peak;
+                  `traffic` is the HBM bytes per launch from committed rocprofv3 counters when they
+                  were taken on the current kernel sources, else null.
+  cpu_baseline  - the float64 CPU oracle timed on this host's cores on the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # MI355X dense MFMA, published
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["scaled_dot_product_fa2_amd/csrc/fa_fwd_kernel.h", "scaled_dot_product_fa2_amd/csrc/fa_layout.h",
+                  "scaled_dot_product_fa2_amd/csrc/fa_api.hip"]
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def flop(w, causal: bool) -> float:
+    f = 4.0 * w.B * w.Hq * w.Nq * w.Nkv * w.D
+    return f / 2 if causal else f
+
+
+def algorithmic_bytes(w) -> int:
+    # Q, K, V read once, O and LSE written once
+    e = 2
+    return e * (2 * w.B * w.Hq * w.Nq * w.D + 2 * w.B * w.Hkv * w.Nkv * w.D) + 4 * w.B * w.Hq * w.Nq
+
+
+def load_traffic(workload: str, mode: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    m = rec.get("modes", {}).get(mode)
+    return None if m is None else m.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, outs):
+    """Time the float64 oracle on this host over the whole workload (both modes) and compare it
+    with the GPU outputs it reproduces."""
+    import numpy as np
+    import oracle
+    workers = min(16, len(os.sched_getaffinity(0)))
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    scale = float(np.float32(w.scale))
+    total_flop, t_total, worst_o, worst_l = 0.0, 0.0, 0.0, 0.0
+    atol, rtol = (1e-2, 1e-2) if w.dtype_name == "bf16" else (2e-3, 2e-3)
+    for causal in w.causal_modes:
+        t0 = time.perf_counter()
+        res, used = oracle.attention_ref_pool(qn, kn, vn, causal=causal, scale=scale, workers=workers)
+        t_total += time.perf_counter() - t0
+        total_flop += flop(w, causal)
+        o_gpu, l_gpu = outs[causal]
+        for (b, h), (o_ref, l_ref) in res.items():
+            og = o_gpu[b, h].double().numpy()
+            worst_o = max(worst_o, float(np.max(np.abs(og - o_ref) / (atol + rtol * np.abs(o_ref)))))
+            worst_l = max(worst_l, float(np.max(np.abs(l_gpu[b, h].double().numpy() - l_ref))))
+    return {"value": total_flop / t_total / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"the whole workload, every (batch, head) in both modes; float64 numpy, one BLAS thread "
+                      f"per worker; {t_total:.2f} s wall",
+            "seconds": round(t_total, 3), "gpu_vs_oracle": {"o_err_ratio_max": round(worst_o, 4),
+                                                          "lse_abs_err_max": worst_l}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="b4h16n1024d128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the attention forward here runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import scaled_dot_product_fa2_amd as fa
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    modes = list(w.causal_modes)
+    outs = {c: (torch.empty(w.B, w.Hq, w.Nq, w.D, dtype=w.dtype, device=dev),
+                torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=dev)) for c in modes}
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(c):
+        fa.fa_fwd(qd, kd, vd, causal=c, out=outs[c][0], lse=outs[c][1], stream=stream)
+
+    for _ in range(args.warmup):
+        for c in modes:
+            launch(c)
+    torch.cuda.synchronize()
+
+    # events bracket every launch on the launch stream (torch's current stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(modes) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, c in enumerate(modes):
+            launch(c)
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_mode_ms = {c: 0.0 for c in modes}
+    for s in range(args.steps):
+        for i, c in enumerate(modes):
+            per_mode_ms[c] += ev[s][i].elapsed_time(ev[s][i + 1])
+    gpu_ms = sum(per_mode_ms.values())
+    ms_per_step = gpu_ms / args.steps
+    total_flop = args.steps * sum(flop(w, c) for c in modes)
+    value = total_flop / (gpu_ms / 1e3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype_name]
+
+    mode_name = {False: "non_causal", True: "causal"}
+    per_mode = {}
+    for c in modes:
+        avg_ms = per_mode_ms[c] / args.steps
+        tf = flop(w, c) / (avg_ms / 1e3) / 1e12
+        per_mode[mode_name[c]] = {"ms_per_launch": round(avg_ms, 5), "tflops": round(tf, 2),
+                                  "frac_of_peak": round(tf / peak, 4)}
+    dominant = max(modes, key=lambda c: per_mode_ms[c])
+    dom_ms = per_mode_ms[dominant] / args.steps
+    achieved = flop(w, dominant) / (dom_ms / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name, mode_name[dominant]),
+                "kernel": f"fa_fwd_kernel<{w.dtype_name}, causal={dominant}, D={w.D}>",
+                "algorithmic_flop_per_launch": flop(w, dominant),
+                "algorithmic_bytes_per_launch": algorithmic_bytes(w)}
+
+    result = {
+        "metric": "attention fwd TFLOP/s (bf16/fp16, causal & non-causal) and % of MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype_name, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D,
+                   "modes": [mode_name[c] for c in modes], "seed": w.seed, "layout": "BNSD",
+                   "kv_storage": w.kv_layout},
+        "frac_of_peak": round(value / peak, 4),
+        "per_mode": per_mode,
+        "roofline": roofline,
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "kernel_sha": kernel_sha(),
+    }
+    if not args.no_cpu_baseline:
+        outs_cpu = {c: (outs[c][0].cpu(), outs[c][1].cpu()) for c in modes}
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, outs_cpu)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
