@@ -45,7 +45,8 @@ extern "C" {
 #define FA_ERR_HEAD_DIM -3  /* D is not one of 16, 32, 64, 128, 256 */
 #define FA_ERR_GQA -4       /* Hkv < 1 or Hq is not a multiple of Hkv */
 #define FA_ERR_SHAPE -5     /* a size is < 1, or a size or an addressed extent overflows */
-#define FA_ERR_LAYOUT -6    /* a d-stride is not 1, or a base address or b/h/n stride is not 16-byte aligned */
+#define FA_ERR_LAYOUT -6    /* a d-stride is not 1, a base address or b/h/n stride is not 16-byte aligned,
+                               a stride is negative, the n-stride exceeds 2^22, or O has a zero stride */
 #define FA_ERR_SCALE -7     /* scale is not a finite number > 0 */
 #define FA_ERR_HIP -8       /* the kernel launch failed (hipGetLastError after the launch) */
 
@@ -62,7 +63,7 @@ extern "C" {
  *       base pointer, multiples of 16 bytes (the kernel moves 16-byte vectors).
  *       Otherwise strides are free (BSND storage viewed as BNSD is fine). Zero
  *       strides (broadcast views) are allowed for Q, K and V, not for O over a
- *       dimension of size > 1.
+ *       dimension of size > 1. The sequence stride must be at most 2^22 elements.
  * scale : score scale, a finite float > 0 (typically 1/sqrt(D)).
  * causal: 0 = every key visible; nonzero = top-left causal mask (key j visible to row i iff j <= i).
  * dtype : FA_DTYPE_F16 or FA_DTYPE_BF16, the element type of q, k, v and o.

@@ -18,14 +18,14 @@ using fa::TileCfg;
 
 // Tile configuration per head dim. Registers: D <= 128 fits two waves per SIMD
 // (two workgroups per CU, 64 KiB of LDS each); D = 256 keeps one wave per SIMD
-// and 128 KiB of LDS per workgroup.
+// with 32-key tiles (64 KiB of LDS per workgroup).
 template <int D>
 struct CfgFor;
 template <> struct CfgFor<16> { typedef TileCfg<16, 4, 1, 64, 2> type; };
 template <> struct CfgFor<32> { typedef TileCfg<32, 4, 1, 64, 2> type; };
 template <> struct CfgFor<64> { typedef TileCfg<64, 4, 1, 64, 2> type; };
 template <> struct CfgFor<128> { typedef TileCfg<128, 4, 1, 64, 2> type; };
-template <> struct CfgFor<256> { typedef TileCfg<256, 4, 1, 64, 1> type; };
+template <> struct CfgFor<256> { typedef TileCfg<256, 4, 1, 32, 1> type; };
 
 struct PlanInfo {
   int threads, bq, bkv, lds;
@@ -80,12 +80,16 @@ int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Largest sequence stride (elements): a tile of up to 256 rows is addressed with 32-bit offsets.
+constexpr int64_t kMaxRowStride = (int64_t)1 << 22;
+
 int check_strides(const int64_t* st, bool is_output, int64_t B, int64_t H, int64_t N) {
   if (st[3] != 1) return FA_ERR_LAYOUT;
   for (int i = 0; i < 3; ++i) {
     if (st[i] < 0) return FA_ERR_LAYOUT;
     if ((st[i] * 2) % 16 != 0) return FA_ERR_LAYOUT;
   }
+  if (st[2] > kMaxRowStride) return FA_ERR_LAYOUT;
   if (is_output) {
     if ((B > 1 && st[0] == 0) || (H > 1 && st[1] == 0) || (N > 1 && st[2] == 0)) return FA_ERR_LAYOUT;
   }

@@ -102,13 +102,11 @@ struct TileCfg {
   static constexpr int THREADS = NW * 64;
   static constexpr int BQ = NW * QB * 32;
   static constexpr int KV_TILE_BYTES = BKV * D * 2;
-  static constexpr int Q_TILE_BYTES = BQ * D * 2;
-  // two stages of K and of V; the Q staging area aliases them before the loop
-  static constexpr int KV_BYTES = 4 * KV_TILE_BYTES;
-  static constexpr int LDS_BYTES = KV_BYTES > Q_TILE_BYTES ? KV_BYTES : Q_TILE_BYTES;
-  static_assert((BKV * chunks_per_row<D>()) % 64 == 0, "a K/V tile must be whole 64-lane copies");
-  static_assert((BQ * chunks_per_row<D>()) % 64 == 0, "a Q tile must be whole 64-lane copies");
-  static_assert(BKV % 32 == 0 && D % 32 == 0 || D == 16, "tile shape");
+  // two stages of K and of V; the Q tile is staged in the same buffers before the key loop
+  static constexpr int LDS_BYTES = 4 * KV_TILE_BYTES;
+  // a tile copy is whole 64-lane instructions, each within one segment column
+  static_assert((BKV * chunks_per_seg<D>()) % 64 == 0, "K/V tile rows must fill whole copy instructions");
+  static_assert(BKV % 32 == 0 && BQ % BKV == 0 && (D % 32 == 0 || D == 16), "tile shape");
 };
 
 __device__ __forceinline__ float wave_half_max(float x) {
@@ -121,23 +119,27 @@ __device__ __forceinline__ float wave_half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Copy `rows` rows (a multiple of 64/chunks_per_row) of a [rows x D] 16-bit tile from global
-// memory into swizzled LDS with direct-to-LDS 16-byte loads. Rows at or past `row_limit` are
-// clamped to the last valid row (their values are never used unmasked).
+// Copy rows [row0, row0 + ROWS) of a [rows x D] 16-bit tensor slice (row stride
+// `stride` bytes) into an LDS tile with direct-to-LDS 16-byte buffer loads; the
+// copy's instructions are spread over the NW waves. The buffer descriptor
+// covers only the valid rows, so rows at or past `n_rows` read as zeros
+// (they are masked out of every result). `lane_off` is dma_lane_offset for this
+// lane and stride; `wave` must be wave-uniform.
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void dma_tile(lds_char_t* lds_tile, const char* gbase, int64_t row_stride_bytes,
-                                         int row0, int row_limit, int wave, int lane) {
-  constexpr int n_inst = ROWS * chunks_per_row<D>() / 64;
+__device__ __forceinline__ void dma_tile(lds_char_t* tile, const char* gbase, int stride, int row0, int n_rows,
+                                         int wave, int lane_off) {
+  constexpr int n_inst = dma_insts<D, ROWS>();
   constexpr int per_wave = (n_inst + NW - 1) / NW;
+  const int valid = n_rows - row0 < ROWS ? n_rows - row0 : ROWS;
+  const uint32_t nbytes = (uint32_t)(valid - 1) * (uint32_t)stride + (uint32_t)(D * 2);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(gbase + (int64_t)row0 * stride), (short)0, (int)nbytes, 0x00020000);
 #pragma unroll
   for (int t = 0; t < per_wave; ++t) {
     const int i = wave + t * NW;
     if (n_inst % NW != 0 && i >= n_inst) break;
-    const RowChunk rc = dma_source<D>(i, lane);
-    int r = row0 + rc.row;
-    r = r < row_limit ? r : row_limit - 1;
-    const char* src = gbase + (int64_t)r * row_stride_bytes + rc.chunk * 16;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(lds_tile + i * 1024), 16, 0, 0);
+    const int soff = (int)dma_inst_offset<D, ROWS>(i, stride);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + i * 1024), 16, lane_off, soff, 0, 0);
   }
 }
 
@@ -145,6 +147,16 @@ __device__ __forceinline__ i32x4 lds_read16(const lds_char_t* p) { return *(cons
 __device__ __forceinline__ i16x4 lds_read_tr(const lds_char_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
 }
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+// Headroom of the lazily updated running maximum, in log2 units: a row's
+// reference maximum is raised (and its accumulator rescaled) only when a tile
+// exceeds it by more than this, so probabilities stay below 2^8.
+constexpr float kRescaleHeadroom = 8.0f;
 
 template <typename T, bool CAUSAL, class Cfg>
 __global__ void __launch_bounds__(Cfg::THREADS)
@@ -156,10 +168,19 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   constexpr int NDB = DPAD ? 1 : D / 32;  // 32-row head-dim blocks of O^T
   constexpr int NKB = BKV / 32;  // 32-row key blocks of S^T
   constexpr int NKS = BKV / 16;  // 16-wide key slices (P.V reduction steps)
+  constexpr int KVB = Cfg::KV_TILE_BYTES;
   typedef typename Elem<T>::vec8 vec8;
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::LDS_BYTES];
-  lds_char_t* const smem = (lds_char_t*)smem_raw;
+  // Four separately declared LDS buffers (K and V, two stages each), so the
+  // compiler can tell a read of one stage from the copy into the other.
+  __shared__ __attribute__((aligned(1024))) char k_st0_raw[KVB];
+  __shared__ __attribute__((aligned(1024))) char k_st1_raw[KVB];
+  __shared__ __attribute__((aligned(1024))) char v_st0_raw[KVB];
+  __shared__ __attribute__((aligned(1024))) char v_st1_raw[KVB];
+  lds_char_t* const k_st0 = (lds_char_t*)k_st0_raw;
+  lds_char_t* const k_st1 = (lds_char_t*)k_st1_raw;
+  lds_char_t* const v_st0 = (lds_char_t*)v_st0_raw;
+  lds_char_t* const v_st1 = (lds_char_t*)v_st1_raw;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -181,29 +202,45 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const char* kbase = (const char*)p.k + ((int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh) * 2;
   const char* vbase = (const char*)p.v + ((int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh) * 2;
 
-  // ---- Q tile: HBM -> LDS (coalesced 16-byte loads), then LDS -> VGPRs in MFMA B-operand layout
-  dma_tile<D, BQ, NW>(smem, qbase, p.q_sn * 2, q0, p.Nq, wave, lane);
+  // Row strides in bytes (validated on the host to keep every tile offset in 31 bits).
+  const int q_stride = (int)(p.q_sn * 2), k_stride = (int)(p.k_sn * 2), v_stride = (int)(p.v_sn * 2);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int k_dma_off = (int)dma_lane_offset<D, false>(lane, k_stride);
+  const int v_dma_off = (int)dma_lane_offset<D, true>(lane, v_stride);
+
+  // ---- Q tile: HBM -> LDS with coalesced 16-byte loads, staged in parts of BKV rows across
+  // the four buffers; then LDS -> VGPRs in the MFMA B-operand layout, kept for the whole key loop.
+  constexpr int Q_PARTS = BQ / BKV;
+  static_assert(Q_PARTS >= 1 && Q_PARTS <= 4 && Q_PARTS * BKV == BQ, "Q tile must fit the four K/V buffers");
+  auto qpart = [&](int part) { return part == 0 ? k_st0 : part == 1 ? k_st1 : part == 2 ? v_st0 : v_st1; };
+  {
+    const int q_dma_off = (int)dma_lane_offset<D, false>(lane, q_stride);
+#pragma unroll
+    for (int part = 0; part < Q_PARTS; ++part)
+      if (q0 + part * BKV < p.Nq)
+        dma_tile<D, BKV, NW>(qpart(part), qbase, q_stride, q0 + part * BKV, p.Nq, wave_u, q_dma_off);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   vec8 qf[QB][NS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wave * QB * 32 + qfrag_row(qb, lane);
+    const lds_char_t* qsrc = qpart(row / BKV);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      i32x4 raw = lds_read16(smem + tile_chunk_offset<D>(row, kfrag_chunk(s, lane)));
-      qf[qb][s] = __builtin_bit_cast(vec8, raw);
-    }
+    for (int s = 0; s < NS; ++s)
+      qf[qb][s] = __builtin_bit_cast(
+          vec8, lds_read16(qsrc + tile_chunk_offset<D, BKV, false>(row % BKV, kfrag_chunk(s, lane))));
   }
   __syncthreads();  // the Q staging area is reused for K/V below
 
-  // LDS stages: K[0], K[1], V[0], V[1]
-  auto k_lds = [&](int stage) { return smem + stage * Cfg::KV_TILE_BYTES; };
-  auto v_lds = [&](int stage) { return smem + (2 + stage) * Cfg::KV_TILE_BYTES; };
-
   const int n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
+  // leading tiles in which every (row, key) pair of the workgroup is visible and in range
+  int n_full = p.Nkv / BKV;
+  if (CAUSAL && (q0 + 1) / BKV < n_full) n_full = (q0 + 1) / BKV;
+  if (n_full > n_tiles) n_full = n_tiles;
 
-  // per-lane softmax state for each query block: running max (log2 units, scaled), partial denominator
+  // per-lane softmax state of each query block: reference maximum (log2 units), partial denominator
   float m_run[QB], l_run[QB];
   f32x16 acc[QB][NDB];
 #pragma unroll
@@ -213,55 +250,67 @@ __global__ void __launch_bounds__(Cfg::THREADS)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x16{};
   }
-  // first and last query row owned by this wave
-  const int wq_first = q0 + wave * QB * 32;
+  const int wq_first = q0 + wave * QB * 32;  // first and last query row owned by this wave
   const int wq_last = wq_first + QB * 32 - 1;
   const float c = p.c;
 
-  dma_tile<D, BKV, NW>(k_lds(0), kbase, p.k_sn * 2, 0, p.Nkv, wave, lane);
-  dma_tile<D, BKV, NW>(v_lds(0), vbase, p.v_sn * 2, 0, p.Nkv, wave, lane);
+  dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, 0, p.Nkv, wave_u, k_dma_off);
+  dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, 0, p.Nkv, wave_u, v_dma_off);
+  // per-lane parts of the fragment read offsets
+  constexpr int KP = kfrag_parities<D>();
+  int k_lane[KP];
+#pragma unroll
+  for (int par = 0; par < KP; ++par) k_lane[par] = kfrag_lane_offset<D, BKV>(par, lane);
+  const int v_lane = vtr_lane_offset<D, BKV>(lane);
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int st = j & 1;
-    const int k0 = j * BKV;
+  // One key tile: wait for its copy, start the next tile's copy into the other stage, then
+  // S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto step = [&](auto stage_c, auto mask_c, int j) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value != 0;
+    lds_char_t* const kcur = S == 0 ? k_st0 : k_st1;
+    lds_char_t* const vcur = S == 0 ? v_st0 : v_st1;
+    lds_char_t* const knext = S == 0 ? k_st1 : k_st0;
+    lds_char_t* const vnext = S == 0 ? v_st1 : v_st0;
+    const int kpos = j * BKV;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (j + 1 < n_tiles) {
-      dma_tile<D, BKV, NW>(k_lds(st ^ 1), kbase, p.k_sn * 2, k0 + BKV, p.Nkv, wave, lane);
-      dma_tile<D, BKV, NW>(v_lds(st ^ 1), vbase, p.v_sn * 2, k0 + BKV, p.Nkv, wave, lane);
+      dma_tile<D, BKV, NW>(knext, kbase, k_stride, kpos + BKV, p.Nkv, wave_u, k_dma_off);
+      dma_tile<D, BKV, NW>(vnext, vbase, v_stride, kpos + BKV, p.Nkv, wave_u, v_dma_off);
     }
-    // A causal tile wholly to the right of this wave's last row contributes nothing.
-    if (CAUSAL && k0 > wq_last) continue;
-    const bool need_mask = (k0 + BKV > p.Nkv) || (CAUSAL && k0 + BKV - 1 > wq_first);
+    // a causal tile wholly to the right of this wave's last row contributes nothing
+    if (CAUSAL && MASK && kpos > wq_last) return;
 
-    // ---- S^T = K Q^T for this tile
+    // ---- S^T = K Q^T
     f32x16 sc[QB][NKB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sc[qb][kb] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int s = 0; s < NS; ++s) {
+      vec8 kf[NKB];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const vec8 kf = __builtin_bit_cast(
-            vec8, lds_read16(k_lds(st) + tile_chunk_offset<D>(kfrag_row(kb, lane), kfrag_chunk(s, lane))));
+      for (int kb = 0; kb < NKB; ++kb)
+        kf[kb] = __builtin_bit_cast(vec8, lds_read16(kcur + k_lane[s % KP] + kfrag_const_offset<D, BKV>(kb, s)));
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = Elem<T>::mfma(kf, qf[qb][s], sc[qb][kb]);
-      }
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = Elem<T>::mfma(kf[kb], qf[qb][s], sc[qb][kb]);
     }
 
-    // ---- online softmax (base 2), per lane = per query row
+    // ---- online softmax in base 2, one query row per lane
     vec8 pf[QB][NKS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const int qrow = wq_first + qfrag_row(qb, lane);
-      if (need_mask) {
+      if (MASK) {
+        const int qrow = wq_first + qfrag_row(qb, lane);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + acc_row(r, lane);
+            const int key = kpos + 32 * kb + acc_row(r, lane);
             const bool hidden = (key >= p.Nkv) || (CAUSAL && key > qrow);
             sc[qb][kb][r] = hidden ? -INFINITY : sc[qb][kb][r];
           }
@@ -271,12 +320,17 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
-      mx = wave_half_max(mx);
-      const float m_new = fmaxf(m_run[qb], mx * c);
-      // m_new is -inf only if every key seen so far is hidden from this row; then keep 0 as the shift
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-      m_run[qb] = m_new;
+      const float mt = wave_half_max(mx) * c;  // tile maximum of the scaled scores, log2 units
+      const bool grow = mt > m_run[qb] + kRescaleHeadroom;
+      if (__any(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.f;
+        m_run[qb] = grow ? mt : m_run[qb];
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
+      }
+      // a row that has seen no visible key yet keeps -inf; its scores are all -inf here too
+      const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -286,12 +340,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           sc[qb][kb][r] = pv;
           rs += pv;
         }
-      l_run[qb] = l_run[qb] * alpha + rs;
-      // rescale the accumulator only when some row's maximum moved (alpha == 1 is exact otherwise)
-      if (!__all(alpha == 1.f)) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
-      }
+      l_run[qb] += rs;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         vec8 t;
@@ -306,12 +355,10 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const lds_char_t* vt = v_lds(st);
         // D = 16 fills only the first 16 rows of the 32-row block; the other lanes read a valid
         // address and contribute zeros.
-        const int col = DPAD ? (vtr_col(db, lane) & 15) : vtr_col(db, lane);
-        i16x4 lo = lds_read_tr(vt + tile_quad_offset<D>(vtr_row(ks, 0, lane), col));
-        i16x4 hi = lds_read_tr(vt + tile_quad_offset<D>(vtr_row(ks, 1, lane), col));
+        i16x4 lo = lds_read_tr(vcur + v_lane + vtr_const_offset<D, BKV>(ks, 0, db));
+        i16x4 hi = lds_read_tr(vcur + v_lane + vtr_const_offset<D, BKV>(ks, 1, db));
         if (DPAD && ((lane >> 4) & 1)) {
           lo = i16x4{};
           hi = i16x4{};
@@ -321,6 +368,23 @@ __global__ void __launch_bounds__(Cfg::THREADS)
         for (int qb = 0; qb < QB; ++qb) acc[qb][db] = Elem<T>::mfma(vf, pf[qb][ks], acc[qb][db]);
       }
     }
+  };
+
+  // unmasked leading tiles two at a time (stage 0 then stage 1), then the masked rest
+  int j = 0;
+  for (; j + 1 < n_full; j += 2) {
+    step(IC<0>(), IC<0>(), j);
+    step(IC<1>(), IC<0>(), j + 1);
+  }
+  if (j < n_full) {
+    step(IC<0>(), IC<0>(), j);
+    ++j;
+  }
+  for (; j < n_tiles; ++j) {
+    if ((j & 1) == 0)
+      step(IC<0>(), IC<1>(), j);
+    else
+      step(IC<1>(), IC<1>(), j);
   }
 
   // ---- epilogue: O = acc / l (rounded once to T), LSE = (m + log2 l) * ln 2
@@ -342,9 +406,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           const int col = 32 * db + acc_row(4 * g4, lane);
           *(i32x2*)(orow + col * 2) = __builtin_bit_cast(i32x2, ov);
         }
-      if (half == 0) {
-        p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] = (m_run[qb] + __log2f(l_tot)) * LN2;
-      }
+      if (half == 0) p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] = (m_run[qb] + __log2f(l_tot)) * LN2;
     }
   }
 }

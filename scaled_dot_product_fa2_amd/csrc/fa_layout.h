@@ -22,54 +22,107 @@
 
 namespace fa {
 
-// 16-byte chunks per tile row of D 16-bit elements.
-template <int D>
-FA_HD constexpr int chunks_per_row() { return D / 8; }
+// ---------------------------------------------------------------------------
+// LDS tile layout. A [ROWS x D] tile of 16-bit elements is stored as columns of
+// row segments: segment column `seg` holds bytes [seg*SEG, (seg+1)*SEG) of every
+// row, rows SEG bytes apart, columns ROWS*SEG bytes apart (SEG = 64 bytes, or
+// 32 for D = 16). LDS serves 64 banks x 4 bytes, so a 256-byte line holds
+// 256/SEG rows of a column and what matters for conflicts is the 16-byte slot.
+//
+// Row tiles (Q and K) are read 16 bytes per lane, one chunk column of 16
+// consecutive rows per access phase; the 16-byte chunks inside a segment are
+// XOR-swizzled with the row's line index so those rows hit 16 distinct slots.
+// Transposed tiles (V) are read with ds_read_b64_tr_b16, 4 consecutive rows x
+// 32 contiguous bytes per 16-lane group; 4 rows of one line already cover 16
+// distinct slots, so they are stored unswizzled.
+//
+// Every address the kernel needs splits into a per-lane part, fixed for the
+// whole kernel, plus a part known at compile time (or uniform across the
+// wave), so LDS accesses use immediate offsets and copies use scalar offsets.
 
-// XOR swizzle of the chunk index within a row: 16 consecutive rows spread over
-// the 16 chunk slots of a 256-byte LDS line, so the 16 lanes that one LDS
-// access phase serves never collide on a bank.
 template <int D>
-FA_HD int chunk_swizzle(int row) {
-  constexpr int cpr = chunks_per_row<D>();
-  constexpr int rows_per_line = cpr >= 16 ? 1 : 16 / cpr;
-  constexpr int slots = cpr >= 16 ? 16 : cpr;
-  return (row / rows_per_line) % slots;
-}
+FA_HD constexpr int seg_bytes() { return D * 2 < 64 ? D * 2 : 64; }
+template <int D>
+FA_HD constexpr int chunks_per_seg() { return seg_bytes<D>() / 16; }
+template <int D>
+FA_HD constexpr int rows_per_line() { return 256 / seg_bytes<D>(); }
 
-// Byte offset of 16-byte chunk c of row `row` inside a tile stored in LDS.
+// Swizzle of the chunk inside a segment for row tiles.
 template <int D>
+FA_HD int row_swizzle(int row) { return (row / rows_per_line<D>()) % chunks_per_seg<D>(); }
+
+// Byte offset of logical 16-byte chunk c (elements 8c .. 8c+7) of row `row`.
+template <int D, int ROWS, bool TR>
 FA_HD int tile_chunk_offset(int row, int c) {
-  return (row * chunks_per_row<D>() + (c ^ chunk_swizzle<D>(row))) * 16;
+  constexpr int cps = chunks_per_seg<D>();
+  const int seg = c / cps, cin = c % cps;
+  const int slot = TR ? cin : (cin ^ row_swizzle<D>(row));
+  return seg * (ROWS * seg_bytes<D>()) + row * seg_bytes<D>() + slot * 16;
 }
 
-// Byte offset of the 8-byte group holding elements [col, col+4) of row `row`
-// (col a multiple of 4).
-template <int D>
+// Byte offset of the 8 bytes holding elements [col, col+4) of row `row` of a
+// transposed tile (col a multiple of 4).
+template <int D, int ROWS>
 FA_HD int tile_quad_offset(int row, int col) {
-  return tile_chunk_offset<D>(row, col / 8) + (col % 8) * 2;
+  return tile_chunk_offset<D, ROWS, true>(row, col / 8) + (col % 8) * 2;
 }
 
-// Direct-to-LDS copy of a tile: instruction `inst` of the copy, lane `lane`.
-// Slot p = 64*inst + lane of the LDS tile holds (row, logical chunk).
+// ---------------------------------------------------------------------------
+// Direct-to-LDS copy of a tile: 64 lanes x 16 bytes per instruction, lane l of
+// instruction i landing at byte 1024*i + 16*l of the tile. Instruction i covers
+// row group rg = i % IPS (64/cps consecutive rows) of segment column i / IPS.
+template <int D, int ROWS>
+FA_HD constexpr int dma_insts() { return ROWS * (D / 8) / 64; }
+
 struct RowChunk {
   int row;
   int chunk;
 };
-template <int D>
+template <int D, int ROWS, bool TR>
 FA_HD RowChunk dma_source(int inst, int lane) {
-  constexpr int cpr = chunks_per_row<D>();
-  const int p = inst * 64 + lane;
-  const int row = p / cpr;
-  const int slot = p % cpr;
-  return RowChunk{row, slot ^ chunk_swizzle<D>(row)};
+  constexpr int cps = chunks_per_seg<D>();
+  constexpr int ips = ROWS * cps / 64;
+  const int seg = inst / ips, rg = inst % ips;
+  const int row = rg * (64 / cps) + lane / cps;
+  const int slot = lane % cps;
+  const int cin = TR ? slot : (slot ^ row_swizzle<D>(row));
+  return RowChunk{row, seg * cps + cin};
+}
+// The byte offset in global memory of dma_source(inst, lane) relative to the
+// tile's first row, split as lane part + instruction part.
+template <int D, bool TR>
+FA_HD int64_t dma_lane_offset(int lane, int64_t row_stride_bytes) {
+  constexpr int cps = chunks_per_seg<D>();
+  const int slot = lane % cps;
+  // row_swizzle of the lane's row depends only on lane / 16 (see dma_source)
+  const int cin = TR ? slot : (slot ^ ((lane / 16) % cps));
+  return (int64_t)(lane / cps) * row_stride_bytes + cin * 16;
+}
+template <int D, int ROWS>
+FA_HD int64_t dma_inst_offset(int inst, int64_t row_stride_bytes) {
+  constexpr int cps = chunks_per_seg<D>();
+  constexpr int ips = ROWS * cps / 64;
+  return (int64_t)((inst % ips) * (64 / cps)) * row_stride_bytes + (inst / ips) * seg_bytes<D>();
 }
 
+// ---------------------------------------------------------------------------
 // MFMA operand fragments (32x32x16 shape).
 // K as the A operand of S^T = K Q^T: lane reads key row (32*kb + lane%32),
 // head-dim chunk 2*s + lane/32 (elements 16*s + 8*(lane/32) .. +7).
 FA_HD int kfrag_row(int kb, int lane) { return 32 * kb + (lane & 31); }
 FA_HD int kfrag_chunk(int s, int lane) { return 2 * s + (lane >> 5); }
+// Split of that read's LDS offset: a per-lane part that depends on the slice
+// only through its parity (s % kfrag_parities), plus a compile-time part.
+template <int D>
+FA_HD constexpr int kfrag_parities() { return chunks_per_seg<D>() / 2; }
+template <int D, int ROWS>
+FA_HD int kfrag_lane_offset(int parity, int lane) {
+  return tile_chunk_offset<D, ROWS, false>(lane & 31, 2 * parity + (lane >> 5));
+}
+template <int D, int ROWS>
+FA_HD int kfrag_const_offset(int kb, int s) {
+  return (2 * s / chunks_per_seg<D>()) * (ROWS * seg_bytes<D>()) + 32 * kb * seg_bytes<D>();
+}
 
 // Q as the B operand: query row (32*qb + lane%32) of the wave's rows, same chunk rule.
 FA_HD int qfrag_row(int qb, int lane) { return 32 * qb + (lane & 31); }
@@ -88,7 +141,8 @@ FA_HD int pv_src_reg(int ks, int e) { return 8 * (ks & 1) + e; }
 
 // V^T as the A operand of O^T = V^T P^T, read with two ds_read_b64_tr_b16.
 // Read `half` (0 or 1) of head-dim block db and key slice ks: lane `lane`
-// supplies the address of V[row][col .. col+3].
+// supplies the address of V[row][col .. col+3]. For D = 16 the column is taken
+// mod 16 (the lanes that would address columns 16..31 carry padding).
 FA_HD int vtr_row(int ks, int half, int lane) {
   const int g = lane >> 4, i = lane & 15;
   return 16 * ks + 8 * half + 4 * (g >> 1) + (i >> 2);
@@ -96,6 +150,15 @@ FA_HD int vtr_row(int ks, int half, int lane) {
 FA_HD int vtr_col(int db, int lane) {
   const int g = lane >> 4, i = lane & 15;
   return 32 * db + 16 * (g & 1) + 4 * (i & 3);
+}
+template <int D>
+FA_HD int vtr_col_clamped(int db, int lane) { return D < 32 ? (vtr_col(db, lane) & 15) : vtr_col(db, lane); }
+// per-lane part and compile-time part of the transposed read's LDS offset
+template <int D, int ROWS>
+FA_HD int vtr_lane_offset(int lane) { return tile_quad_offset<D, ROWS>(vtr_row(0, 0, lane), vtr_col_clamped<D>(0, lane)); }
+template <int D, int ROWS>
+FA_HD int vtr_const_offset(int ks, int half, int db) {
+  return (16 * ks + 8 * half) * seg_bytes<D>() + db * (ROWS * seg_bytes<D>());
 }
 
 // Key tiles a query tile [q0, q0 + bq) visits: all of [0, Nkv) without the mask;

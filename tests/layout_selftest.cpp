@@ -30,35 +30,41 @@ struct Elt {
   int row, col;
 };
 
-template <int D>
-std::vector<Elt> dma_image(int rows) {
-  const int cpr = fa::chunks_per_row<D>();
-  const int n_inst = rows * cpr / 64;
-  std::vector<Elt> lds(rows * D, Elt{-1, -1});
+template <int D, int ROWS, bool TR>
+std::vector<Elt> dma_image() {
+  const int n_inst = fa::dma_insts<D, ROWS>();
+  std::vector<Elt> lds(ROWS * D, Elt{-1, -1});
   std::set<std::pair<int, int>> seen;
+  const int64_t stride = 1000 * 16;  // any row stride: checks the lane/instruction split of the source
   for (int inst = 0; inst < n_inst; ++inst)
     for (int lane = 0; lane < 64; ++lane) {
-      fa::RowChunk rc = fa::dma_source<D>(inst, lane);
-      CHECK(rc.row >= 0 && rc.row < rows && rc.chunk >= 0 && rc.chunk < cpr, "dma source out of tile D=%d", D);
+      fa::RowChunk rc = fa::dma_source<D, ROWS, TR>(inst, lane);
+      CHECK(rc.row >= 0 && rc.row < ROWS && rc.chunk >= 0 && rc.chunk < D / 8, "dma source out of tile D=%d", D);
       CHECK(seen.insert({rc.row, rc.chunk}).second, "dma copies a chunk twice D=%d", D);
-      const int byte = inst * 1024 + lane * 16;  // where global_load_lds puts this lane's 16 bytes
-      CHECK(byte == fa::tile_chunk_offset<D>(rc.row, rc.chunk), "dma slot != tile_chunk_offset D=%d", D);
+      const int byte = inst * 1024 + lane * 16;  // where the direct-to-LDS load puts this lane's 16 bytes
+      CHECK(byte == (fa::tile_chunk_offset<D, ROWS, TR>(rc.row, rc.chunk)), "dma slot != tile_chunk_offset D=%d", D);
+      const int64_t src = fa::dma_lane_offset<D, TR>(lane, stride) + fa::dma_inst_offset<D, ROWS>(inst, stride);
+      CHECK(src == rc.row * stride + rc.chunk * 16, "dma source offset split D=%d", D);
       for (int e = 0; e < 8; ++e) lds[byte / 2 + e] = Elt{rc.row, rc.chunk * 8 + e};
     }
-  CHECK((int)seen.size() == rows * cpr, "dma misses chunks D=%d", D);
+  CHECK((int)seen.size() == ROWS * D / 8, "dma misses chunks D=%d", D);
   return lds;
 }
 
 template <int D>
 void check_d() {
-  const int BKV = 64;
-  std::vector<Elt> lds = dma_image<D>(BKV);
+  constexpr int BKV = 64;
+  std::vector<Elt> lds = dma_image<D, BKV, false>();
+  std::vector<Elt> vlds = dma_image<D, BKV, true>();
   const int NS = D / 16;
   // K fragment (A operand of S^T = K Q^T): lane l must hold K[32kb + l%32][16s + 8(l/32) + e]
   for (int kb = 0; kb < BKV / 32; ++kb)
     for (int s = 0; s < NS; ++s)
       for (int lane = 0; lane < 64; ++lane) {
-        const int byte = fa::tile_chunk_offset<D>(fa::kfrag_row(kb, lane), fa::kfrag_chunk(s, lane));
+        const int byte = fa::tile_chunk_offset<D, BKV, false>(fa::kfrag_row(kb, lane), fa::kfrag_chunk(s, lane));
+        const int split = fa::kfrag_lane_offset<D, BKV>(s % fa::kfrag_parities<D>(), lane) +
+                          fa::kfrag_const_offset<D, BKV>(kb, s);
+        CHECK(byte == split, "K offset split D=%d", D);
         for (int e = 0; e < 8; ++e) {
           const Elt x = lds[byte / 2 + e];
           CHECK(x.row == 32 * kb + lane % 32 && x.col == 16 * s + 8 * (lane / 32) + e, "K frag D=%d", D);
@@ -72,34 +78,41 @@ void check_d() {
       for (int half = 0; half < 2; ++half) {
         int addr[64];
         for (int lane = 0; lane < 64; ++lane) {
-          int col = fa::vtr_col(db, lane);
-          if (D < 32) col &= 15;
-          addr[lane] = fa::tile_quad_offset<D>(fa::vtr_row(ks, half, lane), col);
+          addr[lane] = fa::tile_quad_offset<D, BKV>(fa::vtr_row(ks, half, lane), fa::vtr_col_clamped<D>(db, lane));
+          const int split = fa::vtr_lane_offset<D, BKV>(lane) + fa::vtr_const_offset<D, BKV>(ks, half, db);
+          CHECK(addr[lane] == split, "V offset split D=%d", D);
           CHECK(addr[lane] % 8 == 0 && addr[lane] >= 0 && addr[lane] + 8 <= BKV * D * 2, "tr addr D=%d", D);
         }
         for (int lane = 0; lane < 64; ++lane) {
           if (D < 32 && ((lane >> 4) & 1)) continue;  // padding lanes are zeroed by the kernel
           for (int e = 0; e < 4; ++e) {
             const int src = 16 * (lane / 16) + 4 * e + (lane % 16) / 4;
-            const Elt x = lds[addr[src] / 2 + (lane % 4)];
+            const Elt x = vlds[addr[src] / 2 + (lane % 4)];
             const int ee = 4 * half + e;
             CHECK(x.row == fa::pv_key(ks, lane, ee) && x.col == 32 * db + lane % 32, "V^T frag D=%d", D);
           }
         }
+        // bank behaviour: each 16-lane group touches 8 chunks on 8 distinct 16-byte slots of the
+        // 256-byte bank line, each 32-lane half 16 distinct slots (D >= 32)
+        for (int span = 16; span <= (D >= 32 ? 32 : 16); span *= 2)
+          for (int g0 = 0; g0 < 64; g0 += span) {
+            std::set<int> slots, chunks;
+            for (int lane = g0; lane < g0 + span; ++lane) {
+              chunks.insert(addr[lane] / 16);
+              slots.insert((addr[lane] / 16) % 16);
+            }
+            CHECK(slots.size() == chunks.size(), "V tr read bank conflict D=%d span=%d", D, span);
+          }
       }
-  // bank behaviour of a 16-byte read phase (16 consecutive lanes): no two lanes on the same
-  // 16-byte slot of a 256-byte line unless they read the same address
-  for (int s = 0; s < NS; ++s)
-    for (int ph = 0; ph < 4; ++ph) {
-      std::map<int, int> slot_addr;
-      for (int lane = 16 * ph; lane < 16 * ph + 16; ++lane) {
-        const int byte = fa::tile_chunk_offset<D>(fa::kfrag_row(0, lane), fa::kfrag_chunk(s, lane));
-        const int slot = (byte / 16) % 16;
-        auto it = slot_addr.find(slot);
-        CHECK(it == slot_addr.end() || it->second == byte || D < 64, "K read bank conflict D=%d", D);
-        slot_addr[slot] = byte;
+  // bank behaviour of the 16-byte fragment reads: the 16 lanes of a phase hit 16 distinct slots
+  for (int kb = 0; kb < BKV / 32; ++kb)
+    for (int s = 0; s < NS; ++s)
+      for (int ph = 0; ph < 4; ++ph) {
+        std::set<int> slots;
+        for (int lane = 16 * ph; lane < 16 * ph + 16; ++lane)
+          slots.insert((fa::tile_chunk_offset<D, BKV, false>(fa::kfrag_row(kb, lane), fa::kfrag_chunk(s, lane)) / 16) % 16);
+        CHECK(slots.size() == 16, "K read bank conflict D=%d", D);
       }
-    }
 }
 
 int main() {

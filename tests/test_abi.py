@@ -86,6 +86,7 @@ BAD = [
     ("odd_row_stride", dict(ks=(8192, 8192, 60, 1)), "FA_ERR_LAYOUT"),
     ("neg_stride", dict(vs=(8192, -8192, 64, 1)), "FA_ERR_LAYOUT"),
     ("zero_out_stride", dict(os=(16384, 0, 64, 1)), "FA_ERR_LAYOUT"),
+    ("huge_row_stride", dict(ks=(1 << 30, 1 << 30, (1 << 22) + 8, 1)), "FA_ERR_LAYOUT"),
     ("misaligned_ptr", dict(k=0x20008), "FA_ERR_LAYOUT"), ("misaligned_lse", dict(lse=0x50002), "FA_ERR_LAYOUT"),
     ("scale_zero", dict(scale=0.0), "FA_ERR_SCALE"), ("scale_neg", dict(scale=-0.1), "FA_ERR_SCALE"),
     ("scale_nan", dict(scale=float("nan")), "FA_ERR_SCALE"), ("scale_inf", dict(scale=float("inf")), "FA_ERR_SCALE"),
