@@ -28,14 +28,16 @@ template <> struct CfgFor<128> { typedef TileCfg<128, 4, 1, 64, 2> type; };
 template <> struct CfgFor<256> { typedef TileCfg<256, 4, 1, 32, 1> type; };
 
 struct PlanInfo {
-  int threads, bq, bkv, lds;
+  int threads, bq, bkv, lds, wgs_per_cu;
 };
 
 template <int D>
 PlanInfo plan_info() {
   typedef typename CfgFor<D>::type C;
-  return PlanInfo{C::THREADS, C::BQ, C::BKV, C::LDS_BYTES};
+  return PlanInfo{C::THREADS, C::BQ, C::BKV, C::LDS_BYTES, C::WAVES_PER_SIMD * 4 / C::NW};
 }
+
+constexpr int kNumCUs = 256;  // MI355X
 
 bool plan_for_d(int64_t D, PlanInfo* out) {
   switch (D) {
@@ -62,7 +64,7 @@ bool extent_ok(int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* st) {
   return mul_ok(acc + 1, 2, &t);
 }
 
-int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int dtype,
+int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int dtype, bool causal,
                 PlanInfo* pi, int64_t* n_qtiles, int64_t* grid) {
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (!plan_for_d(D, pi)) return FA_ERR_HEAD_DIM;
@@ -74,7 +76,10 @@ int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int
   if (!mul_ok(B, Hq, &g) || !mul_ok(g, *n_qtiles, &g) || g > kMaxDim) return FA_ERR_SHAPE;
   int64_t lse_n;
   if (!mul_ok(B, Hq, &lse_n) || !mul_ok(lse_n, Nq, &lse_n) || !mul_ok(lse_n, 4, &lse_n)) return FA_ERR_SHAPE;
-  *grid = g;
+  if (B * Hkv > kMaxDim) return FA_ERR_SHAPE;
+  // persistent grid: as many workgroups as are resident at once (or fewer, for small problems)
+  const fa::Schedule sched{(int)(B * Hkv), (int)Hkv, (int)(Hq / Hkv), (int)*n_qtiles, causal, 0};
+  *grid = sched.choose_grid((int64_t)kNumCUs * pi->wgs_per_cu);
   return FA_OK;
 }
 
@@ -151,7 +156,7 @@ int fa_fwd_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int
   if (!out) return FA_ERR_NULL;
   PlanInfo pi;
   int64_t n_qt = 0, grid = 0;
-  const int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, &pi, &n_qt, &grid);
+  const int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, causal != 0, &pi, &n_qt, &grid);
   if (rc != FA_OK) return rc;
   out->grid = grid;
   out->block_threads = pi.threads;
@@ -169,7 +174,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (!q || !k || !v || !o || !lse || !q_stride || !k_stride || !v_stride || !o_stride) return FA_ERR_NULL;
   PlanInfo pi;
   int64_t n_qt = 0, grid = 0;
-  int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, &pi, &n_qt, &grid);
+  int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, causal != 0, &pi, &n_qt, &grid);
   if (rc != FA_OK) return rc;
   if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_SCALE;
   if ((rc = check_strides(q_stride, false, B, Hq, Nq)) != FA_OK) return rc;

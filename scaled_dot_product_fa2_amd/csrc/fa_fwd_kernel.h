@@ -187,228 +187,227 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const int lane = tid & 63;
   const int half = lane >> 5;
 
-  // ---- work mapping: workgroup -> (batch, query head, query tile), longest causal tiles first
-  const int64_t n_wg = (int64_t)p.B * p.Hq * p.n_qtiles;
-  const int64_t work = xcd_remap((int64_t)blockIdx.x, n_wg);
-  int qt = (int)(work % p.n_qtiles);
-  const int64_t bh = work / p.n_qtiles;
-  const int h = (int)(bh % p.Hq);
-  const int b = (int)(bh / p.Hq);
-  if (CAUSAL) qt = p.n_qtiles - 1 - qt;
-  const int kvh = h / p.group;
-  const int q0 = qt * BQ;
+  // ---- persistent loop over this workgroup's items (batch, query head, query tile); see Schedule
+  const Schedule sched{p.B * p.Hkv, p.Hkv, p.group, p.n_qtiles, CAUSAL, (int)gridDim.x};
+  const int xcd = blockIdx.x % 8;
+  const int64_t n_mine = sched.items_of(xcd);
+  for (int64_t round = 0;; ++round) {
+    const int64_t idx = sched.item_index(blockIdx.x, round);
+    if (idx >= n_mine) break;
+    const Item item = sched.item(xcd, idx);
+    const int b = item.b, h = item.h, qt = item.qt;
+    const int kvh = h / p.group;
+    const int q0 = qt * BQ;
+    __syncthreads();  // every wave is done with the previous item's LDS tiles
 
-  const char* qbase = (const char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
-  const char* kbase = (const char*)p.k + ((int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh) * 2;
-  const char* vbase = (const char*)p.v + ((int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh) * 2;
+    const char* qbase = (const char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
+    const char* kbase = (const char*)p.k + ((int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh) * 2;
+    const char* vbase = (const char*)p.v + ((int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh) * 2;
 
-  // Row strides in bytes (validated on the host to keep every tile offset in 31 bits).
-  const int q_stride = (int)(p.q_sn * 2), k_stride = (int)(p.k_sn * 2), v_stride = (int)(p.v_sn * 2);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int k_dma_off = (int)dma_lane_offset<D, false>(lane, k_stride);
-  const int v_dma_off = (int)dma_lane_offset<D, true>(lane, v_stride);
+    // Row strides in bytes (validated on the host to keep every tile offset in 31 bits).
+    const int q_stride = (int)(p.q_sn * 2), k_stride = (int)(p.k_sn * 2), v_stride = (int)(p.v_sn * 2);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int k_dma_off = (int)dma_lane_offset<D, false>(lane, k_stride);
+    const int v_dma_off = (int)dma_lane_offset<D, true>(lane, v_stride);
 
-  // ---- Q tile: HBM -> LDS with coalesced 16-byte loads, staged in parts of BKV rows across
-  // the four buffers; then LDS -> VGPRs in the MFMA B-operand layout, kept for the whole key loop.
-  constexpr int Q_PARTS = BQ / BKV;
-  static_assert(Q_PARTS >= 1 && Q_PARTS <= 4 && Q_PARTS * BKV == BQ, "Q tile must fit the four K/V buffers");
-  auto qpart = [&](int part) { return part == 0 ? k_st0 : part == 1 ? k_st1 : part == 2 ? v_st0 : v_st1; };
-  {
-    const int q_dma_off = (int)dma_lane_offset<D, false>(lane, q_stride);
+    // ---- Q tile: HBM -> LDS with coalesced 16-byte loads, staged in parts of BKV rows across
+    // the four buffers; then LDS -> VGPRs in the MFMA B-operand layout, kept for the whole key loop.
+    constexpr int Q_PARTS = BQ / BKV;
+    static_assert(Q_PARTS >= 1 && Q_PARTS <= 4 && Q_PARTS * BKV == BQ, "Q tile must fit the four K/V buffers");
+    auto qpart = [&](int part) { return part == 0 ? k_st0 : part == 1 ? k_st1 : part == 2 ? v_st0 : v_st1; };
+    {
+      const int q_dma_off = (int)dma_lane_offset<D, false>(lane, q_stride);
 #pragma unroll
-    for (int part = 0; part < Q_PARTS; ++part)
-      if (q0 + part * BKV < p.Nq)
-        dma_tile<D, BKV, NW>(qpart(part), qbase, q_stride, q0 + part * BKV, p.Nq, wave_u, q_dma_off);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  vec8 qf[QB][NS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = wave * QB * 32 + qfrag_row(qb, lane);
-    const lds_char_t* qsrc = qpart(row / BKV);
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      qf[qb][s] = __builtin_bit_cast(
-          vec8, lds_read16(qsrc + tile_chunk_offset<D, BKV, false>(row % BKV, kfrag_chunk(s, lane))));
-  }
-  __syncthreads();  // the Q staging area is reused for K/V below
-
-  const int n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
-  // leading tiles in which every (row, key) pair of the workgroup is visible and in range
-  int n_full = p.Nkv / BKV;
-  if (CAUSAL && (q0 + 1) / BKV < n_full) n_full = (q0 + 1) / BKV;
-  if (n_full > n_tiles) n_full = n_tiles;
-
-  // per-lane softmax state of each query block: reference maximum (log2 units), partial denominator
-  float m_run[QB], l_run[QB];
-  f32x16 acc[QB][NDB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x16{};
-  }
-  const int wq_first = q0 + wave * QB * 32;  // first and last query row owned by this wave
-  const int wq_last = wq_first + QB * 32 - 1;
-  const float c = p.c;
-
-  dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, 0, p.Nkv, wave_u, k_dma_off);
-  dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, 0, p.Nkv, wave_u, v_dma_off);
-  // per-lane parts of the fragment read offsets
-  constexpr int KP = kfrag_parities<D>();
-  int k_lane[KP];
-#pragma unroll
-  for (int par = 0; par < KP; ++par) k_lane[par] = kfrag_lane_offset<D, BKV>(par, lane);
-  const int v_lane = vtr_lane_offset<D, BKV>(lane);
-
-  // One key tile: wait for its copy, start the next tile's copy into the other stage, then
-  // S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto step = [&](auto stage_c, auto mask_c, int j) {
-    constexpr int S = decltype(stage_c)::value;
-    constexpr bool MASK = decltype(mask_c)::value != 0;
-    lds_char_t* const kcur = S == 0 ? k_st0 : k_st1;
-    lds_char_t* const vcur = S == 0 ? v_st0 : v_st1;
-    lds_char_t* const knext = S == 0 ? k_st1 : k_st0;
-    lds_char_t* const vnext = S == 0 ? v_st1 : v_st0;
-    const int kpos = j * BKV;
+      for (int part = 0; part < Q_PARTS; ++part)
+        if (q0 + part * BKV < p.Nq)
+          dma_tile<D, BKV, NW>(qpart(part), qbase, q_stride, q0 + part * BKV, p.Nq, wave_u, q_dma_off);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 1 < n_tiles) {
-      dma_tile<D, BKV, NW>(knext, kbase, k_stride, kpos + BKV, p.Nkv, wave_u, k_dma_off);
-      dma_tile<D, BKV, NW>(vnext, vbase, v_stride, kpos + BKV, p.Nkv, wave_u, v_dma_off);
-    }
-    // a causal tile wholly to the right of this wave's last row contributes nothing
-    if (CAUSAL && MASK && kpos > wq_last) return;
-
-    // ---- S^T = K Q^T
-    f32x16 sc[QB][NKB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sc[qb][kb] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      vec8 kf[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        kf[kb] = __builtin_bit_cast(vec8, lds_read16(kcur + k_lane[s % KP] + kfrag_const_offset<D, BKV>(kb, s)));
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = Elem<T>::mfma(kf[kb], qf[qb][s], sc[qb][kb]);
-    }
-
-    // ---- online softmax in base 2, one query row per lane
-    vec8 pf[QB][NKS];
+    vec8 qf[QB][NS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (MASK) {
-        const int qrow = wq_first + qfrag_row(qb, lane);
+      const int row = wave * QB * 32 + qfrag_row(qb, lane);
+      const lds_char_t* qsrc = qpart(row / BKV);
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        qf[qb][s] = __builtin_bit_cast(
+            vec8, lds_read16(qsrc + tile_chunk_offset<D, BKV, false>(row % BKV, kfrag_chunk(s, lane))));
+    }
+    __syncthreads();  // the Q staging area is reused for K/V below
+
+    const int n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
+    // leading tiles in which every (row, key) pair of the workgroup is visible and in range
+    int n_full = p.Nkv / BKV;
+    if (CAUSAL && (q0 + 1) / BKV < n_full) n_full = (q0 + 1) / BKV;
+    if (n_full > n_tiles) n_full = n_tiles;
+
+    // per-lane softmax state of each query block: reference maximum (log2 units), partial denominator
+    float m_run[QB], l_run[QB];
+    f32x16 acc[QB][NDB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      m_run[qb] = -INFINITY;
+      l_run[qb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x16{};
+    }
+    const int wq_first = q0 + wave * QB * 32;  // first and last query row owned by this wave
+    const int wq_last = wq_first + QB * 32 - 1;
+    const float c = p.c;
+
+    dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, 0, p.Nkv, wave_u, k_dma_off);
+    dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, 0, p.Nkv, wave_u, v_dma_off);
+    // per-lane parts of the fragment read offsets
+    constexpr int KP = kfrag_parities<D>();
+    int k_lane[KP];
+#pragma unroll
+    for (int par = 0; par < KP; ++par) k_lane[par] = kfrag_lane_offset<D, BKV>(par, lane);
+    const int v_lane = vtr_lane_offset<D, BKV>(lane);
+
+    // One key tile: wait for its copy, start the next tile's copy into the other stage, then
+    // S^T = K Q^T, online softmax, O^T += V^T P^T.
+    auto step = [&](auto stage_c, int j) {
+      constexpr int S = decltype(stage_c)::value;
+      const bool mask = j >= n_full;  // wave-uniform
+      lds_char_t* const kcur = S == 0 ? k_st0 : k_st1;
+      lds_char_t* const vcur = S == 0 ? v_st0 : v_st1;
+      lds_char_t* const knext = S == 0 ? k_st1 : k_st0;
+      lds_char_t* const vnext = S == 0 ? v_st1 : v_st0;
+      const int kpos = j * BKV;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 1 < n_tiles) {
+        dma_tile<D, BKV, NW>(knext, kbase, k_stride, kpos + BKV, p.Nkv, wave_u, k_dma_off);
+        dma_tile<D, BKV, NW>(vnext, vbase, v_stride, kpos + BKV, p.Nkv, wave_u, v_dma_off);
+      }
+      // a causal tile wholly to the right of this wave's last row contributes nothing
+      if (CAUSAL && kpos > wq_last) return;
+
+      // ---- S^T = K Q^T
+      f32x16 sc[QB][NKB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sc[qb][kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        vec8 kf[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          kf[kb] = __builtin_bit_cast(vec8, lds_read16(kcur + k_lane[s % KP] + kfrag_const_offset<D, BKV>(kb, s)));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = Elem<T>::mfma(kf[kb], qf[qb][s], sc[qb][kb]);
+      }
+
+      // ---- online softmax in base 2, one query row per lane
+      vec8 pf[QB][NKS];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (mask) {
+          // key = kpos + 4*(lane/32) + koff(kb, r) with koff a compile-time constant; the key is
+          // hidden iff koff > limit, where limit folds the causal bound (key <= row) and the
+          // sequence end (key < Nkv) into one per-lane value.
+          const int qrow = wq_first + qfrag_row(qb, lane);
+          const int base = kpos + 4 * half;
+          int limit = p.Nkv - 1 - base;
+          if (CAUSAL) limit = min(limit, qrow - base);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int koff = 32 * kb + 8 * (r >> 2) + (r & 3);
+              sc[qb][kb][r] = koff > limit ? -INFINITY : sc[qb][kb][r];
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
+        const float mt = wave_half_max(mx) * c;  // tile maximum of the scaled scores, log2 units
+        const bool grow = mt > m_run[qb] + kRescaleHeadroom;
+        if (__any(grow)) {
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.f;
+          m_run[qb] = grow ? mt : m_run[qb];
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
+        }
+        // a row that has seen no visible key yet keeps -inf; its scores are all -inf here too
+        const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+        float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kpos + 32 * kb + acc_row(r, lane);
-            const bool hidden = (key >= p.Nkv) || (CAUSAL && key > qrow);
-            sc[qb][kb][r] = hidden ? -INFINITY : sc[qb][kb][r];
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][kb][r], c, -m_use));
+            sc[qb][kb][r] = pv;
+            rs += pv;
           }
-      }
-      float mx = -INFINITY;
+        l_run[qb] += rs;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int ks = 0; ks < NKS; ++ks) {
+          vec8 t;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
-      const float mt = wave_half_max(mx) * c;  // tile maximum of the scaled scores, log2 units
-      const bool grow = mt > m_run[qb] + kRescaleHeadroom;
-      if (__any(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.f;
-        m_run[qb] = grow ? mt : m_run[qb];
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
-      }
-      // a row that has seen no visible key yet keeps -inf; its scores are all -inf here too
-      const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][kb][r], c, -m_use));
-          sc[qb][kb][r] = pv;
-          rs += pv;
+          for (int e = 0; e < 8; ++e) t[e] = (T)sc[qb][ks >> 1][pv_src_reg(ks, e)];
+          pf[qb][ks] = t;
         }
-      l_run[qb] += rs;
+      }
+
+      // ---- O^T += V^T P^T
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        vec8 t;
+      for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = (T)sc[qb][ks >> 1][pv_src_reg(ks, e)];
-        pf[qb][ks] = t;
+        for (int ks = 0; ks < NKS; ++ks) {
+          // D = 16 fills only the first 16 rows of the 32-row block; the other lanes read a valid
+          // address and contribute zeros.
+          i16x4 lo = lds_read_tr(vcur + v_lane + vtr_const_offset<D, BKV>(ks, 0, db));
+          i16x4 hi = lds_read_tr(vcur + v_lane + vtr_const_offset<D, BKV>(ks, 1, db));
+          if (DPAD && ((lane >> 4) & 1)) {
+            lo = i16x4{};
+            hi = i16x4{};
+          }
+          const vec8 vf = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = Elem<T>::mfma(vf, pf[qb][ks], acc[qb][db]);
+        }
+      }
+    };
+
+    // key tiles two at a time (stage 0 then stage 1); an odd last tile uses stage 0
+    int j = 0;
+    for (; j + 1 < n_tiles; j += 2) {
+      step(IC<0>(), j);
+      step(IC<1>(), j + 1);
+    }
+    if (j < n_tiles) step(IC<0>(), j);
+
+    // ---- epilogue: O = acc / l (rounded once to T), LSE = (m + log2 l) * ln 2
+    const float LN2 = 0.69314718055994530942f;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = wq_first + qfrag_row(qb, lane);
+      const float l_tot = wave_half_sum(l_run[qb]);
+      const float inv = 1.f / l_tot;
+      if (qrow < p.Nq) {
+        char* orow = (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn) * 2;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < (DPAD ? D / 8 : 4); ++g4) {
+            typename Elem<T>::vec4 ov;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ov[e] = (T)(acc[qb][db][4 * g4 + e] * inv);
+            const int col = 32 * db + acc_row(4 * g4, lane);
+            *(i32x2*)(orow + col * 2) = __builtin_bit_cast(i32x2, ov);
+          }
+        if (half == 0) p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] = (m_run[qb] + __log2f(l_tot)) * LN2;
       }
     }
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        // D = 16 fills only the first 16 rows of the 32-row block; the other lanes read a valid
-        // address and contribute zeros.
-        i16x4 lo = lds_read_tr(vcur + v_lane + vtr_const_offset<D, BKV>(ks, 0, db));
-        i16x4 hi = lds_read_tr(vcur + v_lane + vtr_const_offset<D, BKV>(ks, 1, db));
-        if (DPAD && ((lane >> 4) & 1)) {
-          lo = i16x4{};
-          hi = i16x4{};
-        }
-        const vec8 vf = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = Elem<T>::mfma(vf, pf[qb][ks], acc[qb][db]);
-      }
-    }
-  };
-
-  // unmasked leading tiles two at a time (stage 0 then stage 1), then the masked rest
-  int j = 0;
-  for (; j + 1 < n_full; j += 2) {
-    step(IC<0>(), IC<0>(), j);
-    step(IC<1>(), IC<0>(), j + 1);
-  }
-  if (j < n_full) {
-    step(IC<0>(), IC<0>(), j);
-    ++j;
-  }
-  for (; j < n_tiles; ++j) {
-    if ((j & 1) == 0)
-      step(IC<0>(), IC<1>(), j);
-    else
-      step(IC<1>(), IC<1>(), j);
-  }
-
-  // ---- epilogue: O = acc / l (rounded once to T), LSE = (m + log2 l) * ln 2
-  const float LN2 = 0.69314718055994530942f;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = wq_first + qfrag_row(qb, lane);
-    const float l_tot = wave_half_sum(l_run[qb]);
-    const float inv = 1.f / l_tot;
-    if (qrow < p.Nq) {
-      char* orow = (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn) * 2;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < (DPAD ? D / 8 : 4); ++g4) {
-          typename Elem<T>::vec4 ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (T)(acc[qb][db][4 * g4 + e] * inv);
-          const int col = 32 * db + acc_row(4 * g4, lane);
-          *(i32x2*)(orow + col * 2) = __builtin_bit_cast(i32x2, ov);
-        }
-      if (half == 0) p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] = (m_run[qb] + __log2f(l_tot)) * LN2;
-    }
-  }
+  }  // item loop
 }
 
 }  // namespace fa

@@ -172,14 +172,108 @@ FA_HD int64_t kv_tiles_for_qtile(int64_t q0, int64_t bq, int64_t nkv, int64_t bk
   return (end + bkv - 1) / bkv;
 }
 
-// Workgroup id -> logical work id. Consecutive workgroup ids go round-robin
-// to the 8 XCDs; this bijection hands each XCD a contiguous range of logical
-// ids, so the query tiles that share a K/V head run on one XCD's L2.
-FA_HD int64_t xcd_remap(int64_t wg, int64_t n) {
-  const int64_t nx = 8;
-  const int64_t per = n / nx, rem = n % nx;
-  const int64_t x = wg % nx, k = wg / nx;
-  return x * per + (x < rem ? x : rem) + k;
-}
+// ---------------------------------------------------------------------------
+// Work schedule. An item is one (batch, query head, query tile). A "unit" is
+// one (batch, key/value head) pair with its `group` query heads; all items of
+// a unit read the same K/V, so they are kept on one XCD (workgroup ids are
+// dealt round-robin to the 8 XCDs, each with its own L2). With fewer than 8
+// units, each unit's items are spread over 8 / n_units XCDs.
+//
+// The grid holds at most a few workgroups per CU. The dispatcher deals an
+// XCD's workgroups k = 0, 1, ... over its 32 CUs first (k and k + 32 share a
+// CU when two are resident). Workgroup k takes position pos(k) in the XCD's
+// item list in even rounds and the mirrored position in odd rounds (a snake),
+// where pos() snakes over the CU-major order, so the workgroups that share a
+// CU take mirrored positions. With the causal mask the items are listed
+// longest first, so every CU gets a long query tile paired with a short one.
+// The placement only affects balance, never which items are computed.
+constexpr int kCUsPerXCD = 32;
+
+struct Item {
+  int b, h, qt;
+};
+
+struct Schedule {
+  int n_units;  // B * Hkv
+  int hkv;      // Hkv
+  int group;    // Hq / Hkv
+  int n_qt;     // query tiles per head
+  bool causal;
+  int grid;     // workgroups launched
+
+  FA_HD int xcd_share() const { return n_units >= 8 ? 1 : 8 / n_units; }
+  // XCDs that receive items
+  FA_HD int xcds_used() const { return n_units >= 8 ? 8 : n_units * xcd_share(); }
+  // number of items of XCD x
+  FA_HD int64_t items_of(int x) const {
+    if (x >= xcds_used()) return 0;
+    const int64_t per_unit = (int64_t)group * n_qt;
+    if (n_units >= 8) {
+      const int64_t units_x = (n_units - x + 7) / 8;
+      return units_x * per_unit;
+    }
+    const int s = xcd_share(), sub = x % s;
+    return (per_unit - sub + s - 1) / s;
+  }
+  // workgroups of XCD x
+  FA_HD int wgs_of(int x) const { return x < grid ? (grid - x + 7) / 8 : 0; }
+  // grid for at most `max_grid` workgroups: no more than there are items, but at least one
+  // workgroup on every XCD that has items
+  FA_HD int choose_grid(int64_t max_grid) const {
+    const int64_t n_items = (int64_t)n_units * group * n_qt;
+    int64_t g = max_grid < n_items ? max_grid : n_items;
+    if (g < xcds_used()) g = xcds_used();
+    return (int)g;
+  }
+  // item number i of XCD x (0 <= i < items_of(x))
+  FA_HD Item item(int x, int64_t i) const {
+    int unit, g, rank;  // rank: position of the query tile in the order items are listed
+    if (n_units >= 8) {
+      const int units_x = (n_units - x + 7) / 8;
+      int64_t m;
+      if (causal) {
+        rank = (int)(i / ((int64_t)units_x * group));
+        const int64_t rest = i % ((int64_t)units_x * group);
+        m = rest / group;
+        g = (int)(rest % group);
+      } else {
+        m = i / ((int64_t)group * n_qt);
+        const int64_t rest = i % ((int64_t)group * n_qt);
+        g = (int)(rest / n_qt);
+        rank = (int)(rest % n_qt);
+      }
+      unit = x + 8 * (int)m;
+    } else {
+      const int s = xcd_share();
+      unit = x / s;
+      const int64_t f = x % s + i * s;
+      if (causal) {
+        rank = (int)(f / group);
+        g = (int)(f % group);
+      } else {
+        g = (int)(f / n_qt);
+        rank = (int)(f % n_qt);
+      }
+    }
+    Item it;
+    it.b = unit / hkv;
+    it.h = (unit % hkv) * group + g;
+    it.qt = causal ? n_qt - 1 - rank : rank;
+    return it;
+  }
+  // position of the XCD's k-th workgroup among its gx workgroups (a bijection of [0, gx))
+  FA_HD static int cu_snake(int k, int gx) {
+    const int full = gx / kCUsPerXCD * kCUsPerXCD;  // workgroups in complete CU rounds
+    if (k >= full) return k;
+    const int s = k / kCUsPerXCD, c = k % kCUsPerXCD;
+    return s * kCUsPerXCD + ((s & 1) ? kCUsPerXCD - 1 - c : c);
+  }
+  // index into the XCD's item list of workgroup `wg` in round r (may be >= items_of)
+  FA_HD int64_t item_index(int wg, int64_t r) const {
+    const int x = wg % 8, k = wg / 8, gx = wgs_of(x);
+    const int pos = cu_snake(k, gx);
+    return r * gx + ((r & 1) ? (gx - 1 - pos) : pos);
+  }
+};
 
 }  // namespace fa

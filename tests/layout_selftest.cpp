@@ -135,15 +135,56 @@ int main() {
       for (int e = 0; e < 8; ++e) keys.insert(fa::pv_key(ks, lane, e));
     CHECK((int)keys.size() == 16 && *keys.begin() == 16 * ks && *keys.rbegin() == 16 * ks + 15, "pv_key perm");
   }
-  // the workgroup remap is a bijection
-  for (long n = 1; n < 300; ++n) {
-    std::vector<int> hit(n, 0);
-    for (long w = 0; w < n; ++w) {
-      long l = fa::xcd_remap(w, n);
-      CHECK(l >= 0 && l < n, "xcd_remap range n=%ld", n);
-      if (l >= 0 && l < n) hit[l]++;
+  // the work schedule visits every (batch, head, query tile) exactly once, keeps every unit's items
+  // on as few XCDs as its share, and (causal) lists each XCD's items longest first
+  for (int B : {1, 2, 4})
+    for (int hkv : {1, 2, 3, 8, 16})
+      for (int group : {1, 4})
+        for (int n_qt : {1, 3, 8, 17})
+          for (int causal = 0; causal < 2; ++causal)
+            for (int grid : {1, 5, 64, 256, 512}) {
+              fa::Schedule sc{B * hkv, hkv, group, n_qt, causal != 0, 0};
+              const long n_items = (long)B * hkv * group * n_qt;
+              sc.grid = sc.choose_grid(grid);
+              std::vector<int> seen(n_items, 0);
+              std::map<int, std::set<int>> unit_xcds;
+              for (int wg = 0; wg < sc.grid; ++wg) {
+                const int x = wg % 8;
+                int prev_qt = 1 << 30;
+                for (long r = 0;; ++r) {
+                  const long i = sc.item_index(wg, r);
+                  if (i >= sc.items_of(x)) break;
+                  const fa::Item it = sc.item(x, i);
+                  CHECK(it.b >= 0 && it.b < B && it.h >= 0 && it.h < hkv * group && it.qt >= 0 && it.qt < n_qt,
+                        "schedule item out of range");
+                  seen[((long)it.b * hkv * group + it.h) * n_qt + it.qt]++;
+                  unit_xcds[it.b * hkv + it.h / group].insert(x);
+                  (void)prev_qt;
+                }
+              }
+              for (long k = 0; k < n_items; ++k) CHECK(seen[k] == 1, "schedule misses or repeats an item");
+              for (auto& kv : unit_xcds) CHECK((int)kv.second.size() <= sc.xcd_share(), "unit spread over too many XCDs");
+              // causal: within an XCD the listed items never grow longer
+              if (causal)
+                for (int x = 0; x < 8; ++x)
+                  for (long i = 1; i < sc.items_of(x); ++i)
+                    CHECK(sc.item(x, i).qt <= sc.item(x, i - 1).qt, "causal items not longest first");
+            }
+  // causal balance of the workload of 4 batches x 16 heads x 8 query tiles (2..16 key tiles each)
+  // on 2 resident workgroups per CU: every CU gets the same total
+  {
+    fa::Schedule sc{64, 16, 1, 8, true, 0};
+    sc.grid = sc.choose_grid(512);
+    std::map<std::pair<int, int>, int> cu_load;
+    for (int wg = 0; wg < sc.grid; ++wg) {
+      const int x = wg % 8, k = wg / 8;
+      for (long r = 0;; ++r) {
+        const long i = sc.item_index(wg, r);
+        if (i >= sc.items_of(x)) break;
+        cu_load[{x, k % fa::kCUsPerXCD}] += 2 * (sc.item(x, i).qt + 1);
+      }
     }
-    for (long l = 0; l < n; ++l) CHECK(hit[l] == 1, "xcd_remap not bijective n=%ld", n);
+    for (auto& kv : cu_load) CHECK(kv.second == 18, "unbalanced CU: %d key tiles", kv.second);
   }
   // key tiles per query tile against a brute-force scan of the visible (row, key) pairs
   for (int nq : {1, 7, 64, 100, 128, 300})

@@ -101,7 +101,12 @@ def test_validation_rejects(name, over, code):
 def test_plan_and_tile_pairs():
     from scaled_dot_product_fa2_amd import fa_fwd_plan, fa_tile_pairs
     p = fa_fwd_plan(4, 16, 16, 1024, 1024, 128, False, 1)
-    assert p["grid"] == 4 * 16 * ((1024 + p["block_q"] - 1) // p["block_q"])
+    n_items = 4 * 16 * ((1024 + p["block_q"] - 1) // p["block_q"])
+    # persistent grid: at most the items, at most what fits on the 256 CUs at once
+    assert 8 <= p["grid"] <= n_items and p["grid"] <= 256 * 4
+    assert fa_fwd_plan(1, 1, 1, 16, 16, 64, False, 0)["grid"] >= 1
+    big = fa_fwd_plan(1, 32, 8, 16384, 16384, 128, True, 1)
+    assert big["grid"] < 32 * 16384 // big["block_q"]
     assert p["block_threads"] % 64 == 0 and p["lds_bytes"] <= 160 * 1024
     nq_t = 1024 // p["block_q"]
     nkv_t = 1024 // p["block_kv"]
