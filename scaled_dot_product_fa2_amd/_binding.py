@@ -86,6 +86,43 @@ def _strides(t: torch.Tensor):
     return (ctypes.c_int64 * 4)(*t.stride())
 
 
+class FaCall:
+    """A validated, pre-marshalled fa_fwd call on fixed tensors: calling it enqueues one forward.
+
+    Built by ``fa_fwd_call``; the ctypes argument tuple is prepared once, so repeated launches cost
+    only the foreign call. The tensors must stay alive and keep their storage while it is used.
+    """
+
+    def __init__(self, args, keepalive):
+        self._fn = load_library().fa_fwd
+        self._args = args
+        self._keepalive = keepalive
+
+    def __call__(self) -> None:
+        code = self._fn(*self._args)
+        if code != 0:
+            raise FaError(code, fa_strerror(code))
+
+
+def fa_fwd_call(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor, *,
+                causal: bool = False, scale: Optional[float] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> FaCall:
+    """Prepare repeated forwards of the same tensors (see FaCall); checks arguments once."""
+    fa_fwd(q, k, v, causal=causal, scale=scale, out=out, lse=lse, stream=stream)  # validates and runs once
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nkv, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    strides = [_strides(t) for t in (q, k, v, out)]
+    args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
+            B, Hq, Hkv, Nq, Nkv, D, *strides, ctypes.c_float(scale), int(bool(causal)), _DTYPES[q.dtype],
+            ctypes.c_void_p(stream.cuda_stream))
+    return FaCall(args, (q, k, v, out, lse, strides))
+
+
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
            lse: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None

@@ -112,3 +112,22 @@ def test_output_padding_untouched():
     ref, _ = fa.fa_fwd(q, k, v, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(view, ref)
+
+
+def test_prepared_call_matches_direct_call():
+    """fa_fwd_call (arguments marshalled once) launches the same forward as fa_fwd."""
+    fa = _fa()
+    q, k, v = workloads.make_random(2, 8, 2, 300, 300, 128, torch.bfloat16, seed=77)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    _announce("prepared call")
+    for causal in (False, True):
+        o = torch.empty_like(q)
+        lse = torch.empty(2, 8, 300, dtype=torch.float32, device=DEV)
+        call = fa.fa_fwd_call(q, k, v, o, lse, causal=causal)
+        o.fill_(float("nan"))
+        call()
+        call()
+        torch.cuda.synchronize()
+        o2, lse2 = fa.fa_fwd(q, k, v, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(lse, lse2)
