@@ -158,6 +158,16 @@ struct IC {
 // exceeds it by more than this, so probabilities stay below 2^8.
 constexpr float kRescaleHeadroom = 8.0f;
 
+// Fragment read-ahead in the two MFMA loops, in head-dim slices of K (S^T) and in V fragments
+// (P V). Left to itself the compiler issues each LDS read right before the MFMA that consumes it,
+// into the same few registers, so every MFMA waits out a full LDS round trip; scheduling-group
+// barriers pin an order with the reads this far ahead instead.
+constexpr int kQkLead = 3;
+constexpr int kPvLead = 4;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 template <typename T, bool CAUSAL, class Cfg>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
@@ -290,16 +300,28 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) sc[qb][kb] = f32x16{};
+      {
+        vec8 kf[NS][NKB];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        vec8 kf[NKB];
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          kf[kb] = __builtin_bit_cast(vec8, lds_read16(kcur + k_lane[s % KP] + kfrag_const_offset<D, BKV>(kb, s)));
+          for (int kb = 0; kb < NKB; ++kb)
+            kf[s][kb] = __builtin_bit_cast(vec8, lds_read16(kcur + k_lane[s % KP] + kfrag_const_offset<D, BKV>(kb, s)));
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = Elem<T>::mfma(kf[kb], qf[qb][s], sc[qb][kb]);
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = Elem<T>::mfma(kf[s][kb], qf[qb][s], sc[qb][kb]);
+        // Issue order: the reads of the first kQkLead slices, then per slice its MFMAs followed by
+        // the reads of slice s + kQkLead, so every MFMA finds its operand already in flight.
+        constexpr int LEAD = kQkLead < NS ? kQkLead : NS;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD * NKB, 0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, NKB * QB, 0);
+          if (s + LEAD < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NKB, 0);
+        }
       }
 
       // ---- online softmax in base 2, one query row per lane
@@ -358,21 +380,36 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       }
 
       // ---- O^T += V^T P^T
+      {
+        vec8 vf[NKS][NDB];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          // D = 16 fills only the first 16 rows of the 32-row block; the other lanes read a valid
-          // address and contribute zeros.
-          i16x4 lo = lds_read_tr(vcur + v_lane + vtr_const_offset<D, BKV>(ks, 0, db));
-          i16x4 hi = lds_read_tr(vcur + v_lane + vtr_const_offset<D, BKV>(ks, 1, db));
-          if (DPAD && ((lane >> 4) & 1)) {
-            lo = i16x4{};
-            hi = i16x4{};
+          for (int db = 0; db < NDB; ++db) {
+            // D = 16 fills only the first 16 rows of the 32-row block; the other lanes read a
+            // valid address and contribute zeros.
+            i16x4 lo = lds_read_tr(vcur + v_lane + vtr_const_offset<D, BKV>(ks, 0, db));
+            i16x4 hi = lds_read_tr(vcur + v_lane + vtr_const_offset<D, BKV>(ks, 1, db));
+            if (DPAD && ((lane >> 4) & 1)) {
+              lo = i16x4{};
+              hi = i16x4{};
+            }
+            vf[ks][db] = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           }
-          const vec8 vf = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = Elem<T>::mfma(vf, pf[qb][ks], acc[qb][db]);
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) acc[qb][db] = Elem<T>::mfma(vf[ks][db], pf[qb][ks], acc[qb][db]);
+        // the same read-ahead for V: two transposing reads per fragment, kPvLead fragments ahead
+        constexpr int NV = NKS * NDB;
+        constexpr int LEAD = kPvLead < NV ? kPvLead : NV;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * LEAD, 0);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, QB, 0);
+          if (i + LEAD < NV) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
         }
       }
     };
