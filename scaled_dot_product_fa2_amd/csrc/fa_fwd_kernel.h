@@ -221,16 +221,26 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     const int v_dma_off = (int)dma_lane_offset<D, true>(lane, v_stride);
 
     // ---- Q tile: HBM -> LDS with coalesced 16-byte loads, staged in parts of BKV rows across
-    // the four buffers; then LDS -> VGPRs in the MFMA B-operand layout, kept for the whole key loop.
+    // the K/V buffers; then LDS -> VGPRs in the MFMA B-operand layout, kept for the whole key loop.
+    // When Q fits the two stage-1 buffers, key/value tile 0 streams into stage 0 at the same time,
+    // so the workgroup pays one memory round trip before its first tile instead of two.
     constexpr int Q_PARTS = BQ / BKV;
     static_assert(Q_PARTS >= 1 && Q_PARTS <= 4 && Q_PARTS * BKV == BQ, "Q tile must fit the four K/V buffers");
-    auto qpart = [&](int part) { return part == 0 ? k_st0 : part == 1 ? k_st1 : part == 2 ? v_st0 : v_st1; };
+    constexpr bool KV0_WITH_Q = Q_PARTS <= 2;
+    auto qpart = [&](int part) {
+      if (KV0_WITH_Q) return part == 0 ? k_st1 : v_st1;
+      return part == 0 ? k_st0 : part == 1 ? k_st1 : part == 2 ? v_st0 : v_st1;
+    };
     {
       const int q_dma_off = (int)dma_lane_offset<D, false>(lane, q_stride);
 #pragma unroll
       for (int part = 0; part < Q_PARTS; ++part)
         if (q0 + part * BKV < p.Nq)
           dma_tile<D, BKV, NW>(qpart(part), qbase, q_stride, q0 + part * BKV, p.Nq, wave_u, q_dma_off);
+      if (KV0_WITH_Q) {
+        dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, 0, p.Nkv, wave_u, k_dma_off);
+        dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, 0, p.Nkv, wave_u, v_dma_off);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -244,7 +254,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
         qf[qb][s] = __builtin_bit_cast(
             vec8, lds_read16(qsrc + tile_chunk_offset<D, BKV, false>(row % BKV, kfrag_chunk(s, lane))));
     }
-    __syncthreads();  // the Q staging area is reused for K/V below
+    __syncthreads();  // the Q staging area takes K/V tiles below
 
     const int n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
     // leading tiles in which every (row, key) pair of the workgroup is visible and in range
@@ -266,8 +276,10 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     const int wq_last = wq_first + QB * 32 - 1;
     const float c = p.c;
 
-    dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, 0, p.Nkv, wave_u, k_dma_off);
-    dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, 0, p.Nkv, wave_u, v_dma_off);
+    if (!KV0_WITH_Q) {
+      dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, 0, p.Nkv, wave_u, k_dma_off);
+      dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, 0, p.Nkv, wave_u, v_dma_off);
+    }
     // per-lane parts of the fragment read offsets
     constexpr int KP = kfrag_parities<D>();
     int k_lane[KP];
@@ -380,6 +392,10 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       }
 
       // ---- O^T += V^T P^T
+      // The wave runs this block at raised issue priority: while it streams P V MFMAs, the other
+      // wave on the SIMD fills the gaps with its softmax or score work instead of competing for
+      // the MFMA pipe.
+      __builtin_amdgcn_s_setprio(1);
       {
         vec8 vf[NKS][NDB];
 #pragma unroll
@@ -412,6 +428,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           if (i + LEAD < NV) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     };
 
     // key tiles two at a time (stage 0 then stage 1); an odd last tile uses stage 0
