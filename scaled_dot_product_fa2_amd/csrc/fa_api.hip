@@ -16,16 +16,17 @@ namespace {
 using fa::FwdParams;
 using fa::TileCfg;
 
-// Tile configuration per head dim. Registers: D <= 128 fits two waves per SIMD
-// (two workgroups per CU, 64 KiB of LDS each); D = 256 keeps one wave per SIMD
-// with 32-key tiles (64 KiB of LDS per workgroup).
+// Tile configuration per head dim: four waves per workgroup, one 32-row query block per wave,
+// and as many waves per SIMD as the registers allow (occupancy is what hides the softmax behind
+// the other waves' MFMAs). D <= 32: four waves per SIMD; D = 64: three; D = 128: two (64 KiB of
+// LDS per workgroup, two per CU); D = 256: two, with 32-key tiles (64 KiB of LDS per workgroup).
 template <int D>
 struct CfgFor;
-template <> struct CfgFor<16> { typedef TileCfg<16, 4, 1, 64, 2> type; };
-template <> struct CfgFor<32> { typedef TileCfg<32, 4, 1, 64, 2> type; };
-template <> struct CfgFor<64> { typedef TileCfg<64, 4, 1, 64, 2> type; };
+template <> struct CfgFor<16> { typedef TileCfg<16, 4, 1, 64, 4> type; };
+template <> struct CfgFor<32> { typedef TileCfg<32, 4, 1, 64, 4> type; };
+template <> struct CfgFor<64> { typedef TileCfg<64, 4, 1, 64, 3> type; };
 template <> struct CfgFor<128> { typedef TileCfg<128, 4, 1, 64, 2> type; };
-template <> struct CfgFor<256> { typedef TileCfg<256, 4, 1, 32, 1> type; };
+template <> struct CfgFor<256> { typedef TileCfg<256, 4, 1, 32, 2> type; };
 
 struct PlanInfo {
   int threads, bq, bkv, lds, wgs_per_cu;

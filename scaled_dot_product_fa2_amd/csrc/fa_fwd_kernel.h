@@ -164,6 +164,7 @@ constexpr float kRescaleHeadroom = 8.0f;
 // barriers pin an order with the reads this far ahead instead.
 constexpr int kQkLead = 3;
 constexpr int kPvLead = 4;
+constexpr int kPvLeadD256 = 3;  // one fragment less at D = 256, which is at the register limit
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -418,9 +419,10 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) acc[qb][db] = Elem<T>::mfma(vf[ks][db], pf[qb][ks], acc[qb][db]);
-        // the same read-ahead for V: two transposing reads per fragment, kPvLead fragments ahead
+        // the same read-ahead for V: two transposing reads per fragment, PV_LEAD fragments ahead
         constexpr int NV = NKS * NDB;
-        constexpr int LEAD = kPvLead < NV ? kPvLead : NV;
+        constexpr int PV_LEAD = D >= 256 ? kPvLeadD256 : kPvLead;
+        constexpr int LEAD = PV_LEAD < NV ? PV_LEAD : NV;
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * LEAD, 0);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
