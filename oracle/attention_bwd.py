@@ -1,0 +1,130 @@
+"""Float64 CPU oracle for the scaled-dot-product attention backward.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: only the test suite and the benchmark's CPU-baseline leg
+use it. It shares no code with the HIP library.
+
+Given the upstream gradient dO of the forward output O, it returns the
+gradients dQ, dK, dV of the loss sum(dO * O) with respect to Q, K and V,
+written out in float64 exactly as the backward is stated in the Ascend notes
+("FlashAttention on Ascend: Triton-Ascend CV pipeline", section 2):
+
+* P is the forward's softmax of the scaled, masked scores, recomputed here
+  from Q and K (the forward definition: scores scale * <q_i, k_j>, top-left
+  causal key set j <= i, row-wise softmax);
+* Delta_i = sum_d O_id * dO_id, with O = P V the exact forward output;
+* dP = dO V^T;
+* dS = scale * P * (dP - Delta), so hidden keys (P = 0) get no gradient;
+* dQ = dS K, dK = dS^T Q, dV = P^T dO.
+
+Readings where the pages leave a point open: the logsumexp the forward also
+returns receives no gradient (only O does); with grouped-query heads the
+query heads that read one key/value head all contribute to its dK and dV,
+which are the sums of their per-head terms (the chain rule through the shared
+tensor); Delta uses the exact O, not a rounded one. No tiling, recomputation
+order or 16-bit rounding of the kernel is emulated.
+
+Query rows are processed in chunks purely to bound memory; the per-row terms
+are independent and dK, dV are sums over rows.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = ["attention_bwd_ref", "head_bwd_ref", "dq_rows"]
+
+
+def _f64(x) -> np.ndarray:
+    a = np.asarray(x)
+    if a.dtype != np.float64:
+        a = a.astype(np.float64)
+    return a
+
+
+def _softmax_rows(qh, kh, r, causal, scale):
+    """P for query rows r of one head: softmax of the scaled scores over the visible keys."""
+    s = scale * (qh[r] @ kh.T)
+    if causal:
+        key_pos = np.arange(kh.shape[0])
+        s = np.where(key_pos[None, :] <= r[:, None], s, -np.inf)  # top-left causal key set
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=1, keepdims=True)
+
+
+def head_bwd_ref(qh, kh, vh, doh, *, causal: bool, scale: float,
+                 row_chunk: int = 512) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of one query head against the key/value head it reads.
+
+    qh: (Nq, D), kh: (Nkv, D), vh: (Nkv, Dv), doh: (Nq, Dv).
+    Returns dq (Nq, D), dk (Nkv, D), dv (Nkv, Dv), float64; dk and dv hold this head's terms.
+    """
+    qh, kh, vh, doh = _f64(qh), _f64(kh), _f64(vh), _f64(doh)
+    dq = np.empty_like(qh)
+    dk = np.zeros_like(kh)
+    dv = np.zeros_like(vh)
+    rows = np.arange(qh.shape[0])
+    for start in range(0, rows.shape[0], row_chunk):
+        r = rows[start:start + row_chunk]
+        p = _softmax_rows(qh, kh, r, causal, scale)      # recomputed probabilities
+        o = p @ vh                                       # exact forward output of these rows
+        delta = np.sum(o * doh[r], axis=1)               # Delta = rowsum(O * dO)
+        dp = doh[r] @ vh.T                               # dP = dO V^T
+        ds = scale * p * (dp - delta[:, None])           # dS = scale * P * (dP - Delta)
+        dq[r] = ds @ kh                                  # dQ = dS K
+        dk += ds.T @ qh[r]                               # dK = dS^T Q
+        dv += p.T @ doh[r]                               # dV = P^T dO
+    return dq, dk, dv
+
+
+def attention_bwd_ref(q, k, v, do, *, causal: bool, scale: Optional[float] = None,
+                      row_chunk: int = 512) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Full attention backward in float64.
+
+    q: (B, Hq, Nq, D); k: (B, Hkv, Nkv, D); v: (B, Hkv, Nkv, Dv); do: (B, Hq, Nq, Dv).
+    ``scale`` defaults to 1/sqrt(D). Returns dq, dk, dv shaped like q, k, v (float64).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    if Nkv < 1:
+        raise ValueError("softmax over an empty key set is undefined")
+    if do.shape != (B, Hq, Nq, v.shape[3]):
+        raise ValueError("do must be shaped like the forward output")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    group = Hq // Hkv
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // group
+            dq[b, h], dkh, dvh = head_bwd_ref(q[b, h], k[b, kvh], v[b, kvh], do[b, h], causal=causal,
+                                              scale=scale, row_chunk=row_chunk)
+            dk[b, kvh] += dkh   # every query head of the group adds its terms
+            dv[b, kvh] += dvh
+    return dq, dk, dv
+
+
+def dq_rows(q, k, v, do, b: int, h: int, rows: Sequence[int], *, causal: bool,
+            scale: Optional[float] = None) -> np.ndarray:
+    """dQ of selected query rows of (batch b, query head h): each row needs only its own
+    scores, so large shapes can be checked on a sample."""
+    Hq, D = q.shape[1], q.shape[3]
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kvh = h // (Hq // Hkv)
+    qh, kh, vh = _f64(q[b, h]), _f64(k[b, kvh]), _f64(v[b, kvh])
+    r = np.asarray(rows, dtype=np.int64)
+    p = _softmax_rows(qh, kh, r, causal, scale)
+    doh = _f64(do[b, h])[r]
+    delta = np.sum((p @ vh) * doh, axis=1)
+    ds = scale * p * (doh @ vh.T - delta[:, None])
+    return ds @ kh
