@@ -1,5 +1,6 @@
 /*
- * fa.h - C ABI of the gfx950 (MI355X) attention-forward library (libfa.so).
+ * fa.h - C ABI of the gfx950 (MI355X) attention library (libfa.so): the fused
+ * forward (fa_fwd) and its backward (fa_bwd).
  *
  * The library computes, for every batch b, query head h and query row i,
  *
@@ -31,7 +32,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 /* Element types of Q, K, V and O (all four share one type). */
 #define FA_DTYPE_F16 0
@@ -40,7 +41,7 @@ extern "C" {
 /* Return codes. 0 is success; every error is negative. A validation error is
  * reported before any HIP call: nothing is enqueued and O/LSE are untouched. */
 #define FA_OK 0
-#define FA_ERR_NULL -1      /* a required pointer (q, k, v, o, lse, a stride array, out) is NULL */
+#define FA_ERR_NULL -1      /* a required pointer (a tensor, lse, delta, a stride array, out) is NULL */
 #define FA_ERR_DTYPE -2     /* dtype is not FA_DTYPE_F16 or FA_DTYPE_BF16 */
 #define FA_ERR_HEAD_DIM -3  /* D is not one of 16, 32, 64, 128, 256 */
 #define FA_ERR_GQA -4       /* Hkv < 1 or Hq is not a multiple of Hkv */
@@ -81,6 +82,44 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
            const int64_t q_stride[4], const int64_t k_stride[4],
            const int64_t v_stride[4], const int64_t o_stride[4],
+           float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_bwd - enqueue the attention backward on `stream` and return: given the
+ * forward's inputs, its output O and logsumexp LSE, and the gradient dO of a
+ * loss with respect to O, write
+ *
+ *     dq = dS K,   dk = dS^T Q,   dv = P^T dO   (per query head; for grouped
+ *                                              heads dk and dv sum the group)
+ *
+ * where P is the forward's softmax (recomputed from Q, K and LSE), dP = dO V^T,
+ * Delta_i = sum_d O_id dO_id and dS = scale * P * (dP - Delta): the backward of
+ * the Ascend notes ("FlashAttention on Ascend: Triton-Ascend CV pipeline",
+ * section 2). LSE receives no gradient. Every gradient element is written once
+ * by one workgroup (no atomics), so results are bitwise reproducible.
+ *
+ * q, k, v, o : the forward's tensors, as in fa_fwd (o with strides o_stride)
+ * lse        : fp32 (B, Hq, Nq) contiguous, natural log, as written by fa_fwd
+ * dout       : dO viewed as (B, Hq, Nq, D) with strides do_stride
+ * dq, dk, dv : outputs, shaped like q, k, v, with strides dq_stride, dk_stride, dv_stride;
+ *              every element is overwritten (no accumulation into existing values)
+ * delta      : caller-provided fp32 workspace of B * Hq * Nq floats (4-byte aligned),
+ *              overwritten with Delta, contiguous (B, Hq, Nq)
+ * scale, causal, dtype, stream, and the stride and alignment rules: as in fa_fwd,
+ *              with o and dout read-only inputs and dq, dk, dv outputs (no zero strides).
+ *
+ * Sizes as in fa_fwd, and B, Hq <= 65535. Ownership: the caller owns every
+ * buffer; outputs and the workspace must not overlap any input or each other.
+ * The library allocates nothing and never synchronises. Three kernels are
+ * enqueued in order (Delta, then dK/dV, then dQ). Validation errors return
+ * before any HIP call with nothing written.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, float* delta,
+           int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+           const int64_t q_stride[4], const int64_t k_stride[4], const int64_t v_stride[4],
+           const int64_t o_stride[4], const int64_t do_stride[4], const int64_t dq_stride[4],
+           const int64_t dk_stride[4], const int64_t dv_stride[4],
            float scale, int causal, int dtype, void* stream);
 
 /* Launch plan of fa_fwd for a shape, computed on the host without any HIP call. */

@@ -1,5 +1,5 @@
 """ctypes binding of libfa.so. Argument marshalling only; every step of the
-attention forward runs in the library's kernels."""
+attention forward and backward runs in the library's kernels."""
 from __future__ import annotations
 
 import ctypes
@@ -45,6 +45,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p, f32, i32,
                            i32, vp]
     lib.fa_fwd.restype = i32
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                           i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f32, i32, i32, vp]
+    lib.fa_bwd.restype = i32
     lib.fa_fwd_plan.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(_Plan)]
     lib.fa_fwd_plan.restype = i32
     lib.fa_tile_pairs.argtypes = [i64, i64, i64, i64, i32]
@@ -162,3 +165,48 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = 
         float(scale), int(bool(causal)), _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return out, lse
+
+
+def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+           dout: torch.Tensor, *, causal: bool = False, scale: Optional[float] = None,
+           dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+           delta: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None
+           ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Attention backward: returns (dq, dk, dv) for the forward (o, lse) = fa_fwd(q, k, v).
+
+    dout is the gradient of the loss with respect to o (same shape and dtype). dq, dk, dv (shaped
+    like q, k, v) and the float32 workspace ``delta`` (contiguous (B, Hq, Nq)) are allocated when
+    not passed. Same dtype, stride and alignment rules as ``fa_fwd``.
+    """
+    if not all(t.is_cuda for t in (q, k, v, o, lse, dout)):
+        raise ValueError("all tensors must be on the GPU")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v, o, dout must share one dtype, float16 or bfloat16")
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nkv, _ = k.shape
+    if k.shape != (B, Hkv, Nkv, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, o and dout")
+    if lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, Hq, Nq) tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError(f"{name} must match the shape, dtype and device of its input")
+    if delta is None:
+        delta = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    elif delta.shape != (B, Hq, Nq) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 (B, Hq, Nq) tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    code = load_library().fa_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+        B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(o), _strides(dout),
+        _strides(dq), _strides(dk), _strides(dv), float(scale), int(bool(causal)), _DTYPES[q.dtype],
+        ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return dq, dk, dv

@@ -1,4 +1,4 @@
-"""Build libfa.so (the gfx950 attention forward) in-tree with hipcc.
+"""Build libfa.so (the gfx950 attention forward and backward) in-tree with hipcc.
 
 Usage: python -m scaled_dot_product_fa2_amd.build
 """
@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 SOURCES = [os.path.join(CSRC, "fa_api.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("fa_fwd_kernel.h", "fa_layout.h")] + [os.path.join(INCLUDE, "fa.h")]
+HEADERS = [os.path.join(CSRC, f) for f in ("fa_fwd_kernel.h", "fa_bwd_kernel.h", "fa_layout.h")] + [os.path.join(INCLUDE, "fa.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

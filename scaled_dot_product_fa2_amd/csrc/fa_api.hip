@@ -1,6 +1,6 @@
-// fa_api.hip - C ABI of the gfx950 attention forward: validation, launch plan,
-// dispatch over (dtype, head_dim, causal) instances. The declarations and the
-// contract of every entry point are in include/fa.h.
+// fa_api.hip - C ABI of the gfx950 attention forward and backward: validation,
+// launch plan, dispatch over (dtype, head_dim, causal) instances. The
+// declarations and the contract of every entry point are in include/fa.h.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -8,6 +8,7 @@
 #include <limits>
 
 #include "fa.h"
+#include "fa_bwd_kernel.h"
 #include "fa_fwd_kernel.h"
 #include "fa_layout.h"
 
@@ -121,6 +122,48 @@ int launch_d(int64_t D, const FwdParams& p, int64_t grid, hipStream_t stream) {
   }
 }
 
+// ---- backward: per head dim, the dK/dV kernel (32 keys per wave, 64-row query tiles) and the
+// dQ kernel (32 query rows per wave, 64-key tiles; 32 at D = 256). D <= 64 fits two waves per SIMD.
+template <int D>
+struct BwdCfgFor {
+  static constexpr int W = D <= 64 ? 2 : 1;
+  typedef fa::BwdCfg<D, 4, 64, W> dkdv;
+  typedef fa::BwdCfg<D, 4, D >= 256 ? 32 : 64, W> dq;
+};
+
+constexpr int64_t kMaxGridYZ = 65535;
+
+template <typename T, bool CAUSAL, int D>
+int launch_bwd(const fa::BwdParams& p, hipStream_t stream) {
+  typedef typename BwdCfgFor<D>::dkdv CK;
+  typedef typename BwdCfgFor<D>::dq CQ;
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
+  hipLaunchKernelGGL((fa::fa_bwd_delta_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                     stream, p);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK>),
+                     dim3((unsigned)((p.Nkv + CK::BW - 1) / CK::BW), (unsigned)p.Hkv, (unsigned)p.B),
+                     dim3(CK::THREADS), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<T, CAUSAL, CQ>),
+                     dim3((unsigned)((p.Nq + CQ::BW - 1) / CQ::BW), (unsigned)p.Hq, (unsigned)p.B),
+                     dim3(CQ::THREADS), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <typename T, bool CAUSAL>
+int launch_bwd_d(int64_t D, const fa::BwdParams& p, hipStream_t stream) {
+  switch (D) {
+    case 16: return launch_bwd<T, CAUSAL, 16>(p, stream);
+    case 32: return launch_bwd<T, CAUSAL, 32>(p, stream);
+    case 64: return launch_bwd<T, CAUSAL, 64>(p, stream);
+    case 128: return launch_bwd<T, CAUSAL, 128>(p, stream);
+    case 256: return launch_bwd<T, CAUSAL, 256>(p, stream);
+    default: return FA_ERR_HEAD_DIM;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -213,6 +256,67 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (dtype == FA_DTYPE_BF16)
     return cz ? launch_d<__bf16, true>(D, p, grid, s) : launch_d<__bf16, false>(D, p, grid, s);
   return cz ? launch_d<_Float16, true>(D, p, grid, s) : launch_d<_Float16, false>(D, p, grid, s);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+           int64_t Nkv, int64_t D, const int64_t q_stride[4], const int64_t k_stride[4],
+           const int64_t v_stride[4], const int64_t o_stride[4], const int64_t do_stride[4],
+           const int64_t dq_stride[4], const int64_t dk_stride[4], const int64_t dv_stride[4], float scale,
+           int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta || !q_stride || !k_stride ||
+      !v_stride || !o_stride || !do_stride || !dq_stride || !dk_stride || !dv_stride)
+    return FA_ERR_NULL;
+  PlanInfo pi;
+  int64_t n_qt = 0, grid = 0;
+  int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, causal != 0, &pi, &n_qt, &grid);
+  if (rc != FA_OK) return rc;
+  if (B > kMaxGridYZ || Hq > kMaxGridYZ) return FA_ERR_SHAPE;
+  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_SCALE;
+  if ((rc = check_strides(q_stride, false, B, Hq, Nq)) != FA_OK) return rc;
+  if ((rc = check_strides(k_stride, false, B, Hkv, Nkv)) != FA_OK) return rc;
+  if ((rc = check_strides(v_stride, false, B, Hkv, Nkv)) != FA_OK) return rc;
+  if ((rc = check_strides(o_stride, false, B, Hq, Nq)) != FA_OK) return rc;
+  if ((rc = check_strides(do_stride, false, B, Hq, Nq)) != FA_OK) return rc;
+  if ((rc = check_strides(dq_stride, true, B, Hq, Nq)) != FA_OK) return rc;
+  if ((rc = check_strides(dk_stride, true, B, Hkv, Nkv)) != FA_OK) return rc;
+  if ((rc = check_strides(dv_stride, true, B, Hkv, Nkv)) != FA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_LAYOUT;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0 || (reinterpret_cast<uintptr_t>(delta) & 3u) != 0)
+    return FA_ERR_LAYOUT;
+  if (!extent_ok(B, Hq, Nq, D, q_stride) || !extent_ok(B, Hkv, Nkv, D, k_stride) ||
+      !extent_ok(B, Hkv, Nkv, D, v_stride) || !extent_ok(B, Hq, Nq, D, o_stride) ||
+      !extent_ok(B, Hq, Nq, D, do_stride) || !extent_ok(B, Hq, Nq, D, dq_stride) ||
+      !extent_ok(B, Hkv, Nkv, D, dk_stride) || !extent_ok(B, Hkv, Nkv, D, dv_stride))
+    return FA_ERR_SHAPE;
+
+  fa::BwdParams p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.delta = delta;
+  p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
+  p.k_sb = k_stride[0]; p.k_sh = k_stride[1]; p.k_sn = k_stride[2];
+  p.v_sb = v_stride[0]; p.v_sh = v_stride[1]; p.v_sn = v_stride[2];
+  p.o_sb = o_stride[0]; p.o_sh = o_stride[1]; p.o_sn = o_stride[2];
+  p.do_sb = do_stride[0]; p.do_sh = do_stride[1]; p.do_sn = do_stride[2];
+  p.dq_sb = dq_stride[0]; p.dq_sh = dq_stride[1]; p.dq_sn = dq_stride[2];
+  p.dk_sb = dk_stride[0]; p.dk_sh = dk_stride[1]; p.dk_sn = dk_stride[2];
+  p.dv_sb = dv_stride[0]; p.dv_sh = dv_stride[1]; p.dv_sn = dv_stride[2];
+  p.B = (int32_t)B;
+  p.Hq = (int32_t)Hq;
+  p.Hkv = (int32_t)Hkv;
+  p.Nq = (int32_t)Nq;
+  p.Nkv = (int32_t)Nkv;
+  p.group = (int32_t)(Hq / Hkv);
+  p.c = (float)((double)scale * 1.4426950408889634074);
+  p.scale = scale;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool cz = causal != 0;
+  if (dtype == FA_DTYPE_BF16)
+    return cz ? launch_bwd_d<__bf16, true>(D, p, s) : launch_bwd_d<__bf16, false>(D, p, s);
+  return cz ? launch_bwd_d<_Float16, true>(D, p, s) : launch_bwd_d<_Float16, false>(D, p, s);
 }
 
 }  // extern "C"

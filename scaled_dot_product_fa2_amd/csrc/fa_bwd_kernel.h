@@ -1,0 +1,446 @@
+// fa_bwd_kernel.h - gfx950 (CDNA4) attention backward: dQ, dK, dV.
+//
+// The gradients follow the backward of the Ascend notes ("FlashAttention on
+// Ascend: Triton-Ascend CV pipeline", section 2): Delta = rowsum(O * dO), the
+// probabilities recomputed from the saved logsumexp, dP = dO V^T,
+// dS = scale * P * (dP - Delta), dQ = dS K, dK = dS^T Q, dV = P^T dO.
+// Following the principle the notes settle on (section 2: every gradient tile
+// written once, no atomics and no cross-program reduction), the work is split
+// by owner:
+//  * fa_bwd_delta_kernel: Delta per query row, fp32, from the 16-bit O and dO;
+//  * fa_bwd_dkdv_kernel: one workgroup per (batch, kv head, 32*NW keys). Each
+//    wave keeps its 32 keys' K and V rows in VGPRs as MFMA operands and streams
+//    the Q and dO tiles of every query head of the group past them, so dK and dV
+//    accumulate in registers and are written once (grouped heads summed there);
+//  * fa_bwd_dq_kernel: one workgroup per (batch, query head, 32*NW rows), the
+//    forward's structure with dO next to Q in VGPRs, streaming K and V tiles;
+//    dQ accumulates in registers and is written once.
+// S and dP are recomputed in both gradient kernels (two extra products against
+// a scheme with atomic dQ updates) in exchange for deterministic results.
+//
+// MI355X mapping (32x32x16 MFMAs, fp32 accumulate; P and dS rounded to the
+// input dtype before they enter an MFMA, like P in the forward):
+//  * dK/dV kernel: S = Q K^T and dP = dO V^T with Q/dO fragments read from LDS
+//    and K/V fragments in VGPRs, so each lane owns one key and holds 16 query
+//    rows; then dV^T += dO^T P and dK^T += Q^T dS take P and dS straight from
+//    those accumulators (the query order of the reduction permuted as the key
+//    order is in the forward's P.V product) against transposing LDS reads of
+//    the dO and Q tiles.
+//  * dQ kernel: S^T = K Q^T and dP^T = V dO^T (each lane owns one query row, as
+//    in the forward), then dQ^T += K^T dS^T with transposing reads of the K tile.
+#pragma once
+
+#include "fa_fwd_kernel.h"
+
+namespace fa {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // natural-log logsumexp of the forward, contiguous (B, Hq, Nq)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace, contiguous (B, Hq, Nq)
+  int64_t q_sb, q_sh, q_sn;  // element strides; the head-dim stride is 1
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t do_sb, do_sh, do_sn;
+  int64_t dq_sb, dq_sh, dq_sn;
+  int64_t dk_sb, dk_sh, dk_sn;
+  int64_t dv_sb, dv_sh, dv_sn;
+  int32_t B, Hq, Hkv, Nq, Nkv;
+  int32_t group;  // Hq / Hkv
+  float c;        // scale * log2(e)
+  float scale;
+};
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Delta_i = sum_d O_id * dO_id for every (batch, head, row), fp32. D/8 lanes per row, one
+// 16-byte vector of O and of dO per lane, then a butterfly sum over those lanes.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const BwdParams p) {
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RPB = 256 / LPR;      // rows per workgroup
+  typedef typename Elem<T>::vec8 vec8;
+  const int tid = threadIdx.x;
+  const int64_t g = (int64_t)blockIdx.x * RPB + tid / LPR;  // row over (B, Hq, Nq)
+  const int64_t total = (int64_t)p.B * p.Hq * p.Nq;
+  float acc = 0.f;
+  if (g < total) {
+    const int i = (int)(g % p.Nq);
+    const int64_t bh = g / p.Nq;
+    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+    const int col = 8 * (tid % LPR);
+    const vec8 o = *(const vec8*)((const T*)p.o + b * p.o_sb + h * p.o_sh + i * p.o_sn + col);
+    const vec8 d = *(const vec8*)((const T*)p.dout + b * p.do_sb + h * p.do_sh + i * p.do_sn + col);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)d[e], acc);
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, LPR);
+  if (g < total && tid % LPR == 0) p.delta[g] = acc;
+}
+
+// Workgroup shape of the gradient kernels: NW waves of 32 rows each (keys for dK/dV, query rows
+// for dQ), tiles of BT rows streamed past them (query rows for dK/dV, keys for dQ).
+template <int D_, int NW_, int BT_, int WAVES_PER_SIMD_>
+struct BwdCfg {
+  static constexpr int D = D_;
+  static constexpr int NW = NW_;
+  static constexpr int BT = BT_;
+  static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int BW = NW * 32;  // rows owned by the workgroup
+  static constexpr int TILE_BYTES = BT * D * 2;
+  static_assert(BT % 32 == 0 && dma_insts<D, BT>() * 64 == BT * (D / 8), "tile rows must fill whole copies");
+};
+
+// ------------------------------------------------------------------------------------------------
+// dK, dV. Grid: (ceil(Nkv / BW), Hkv, B).
+template <typename T, bool CAUSAL, class Cfg>
+__global__ void __launch_bounds__(Cfg::THREADS)
+    __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
+    fa_bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int D = Cfg::D, NW = Cfg::NW, BQ = Cfg::BT, BK = Cfg::BW;
+  constexpr int NS = D / 16;
+  constexpr bool DPAD = D < 32;
+  constexpr int NDB = DPAD ? 1 : D / 32;
+  constexpr int NQB = BQ / 32;  // 32-row query blocks per tile
+  constexpr int TB = Cfg::TILE_BYTES;
+  typedef typename Elem<T>::vec8 vec8;
+
+  // Q and dO tiles in the transposing layout (read both as row fragments and transposed), two
+  // stages each, plus the tile's logsumexp and Delta.
+  __shared__ __attribute__((aligned(1024))) char q_st0_raw[TB];
+  __shared__ __attribute__((aligned(1024))) char q_st1_raw[TB];
+  __shared__ __attribute__((aligned(1024))) char o_st0_raw[TB];
+  __shared__ __attribute__((aligned(1024))) char o_st1_raw[TB];
+  __shared__ __attribute__((aligned(256))) float ls_st0[BQ];
+  __shared__ __attribute__((aligned(256))) float ls_st1[BQ];
+  __shared__ __attribute__((aligned(256))) float dl_st0[BQ];
+  __shared__ __attribute__((aligned(256))) float dl_st1[BQ];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int k0 = blockIdx.x * BK;
+  const int kw0 = k0 + 32 * wave;  // first key of this wave
+  const int my_key = kw0 + (lane & 31);
+
+  // K and V rows of the wave's keys as B operands: lane holds row (lane % 32), elements
+  // 16*s + 8*(lane/32) .. +7. Keys past Nkv read as zero.
+  vec8 kf[NS], vf[NS];
+  {
+    const T* krow = (const T*)p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)my_key * p.k_sn;
+    const T* vrow = (const T*)p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)my_key * p.v_sn;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int col = 16 * s + 8 * (lane >> 5);
+      kf[s] = my_key < p.Nkv ? *(const vec8*)(krow + col) : vec8{};
+      vf[s] = my_key < p.Nkv ? *(const vec8*)(vrow + col) : vec8{};
+    }
+  }
+  f32x16 dkT[NDB], dvT[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dkT[db] = f32x16{};
+    dvT[db] = f32x16{};
+  }
+
+  // Work list: (query head of the group, query tile), tiles that can see one of the keys only.
+  const int n_qt = (p.Nq + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? (k0 / BQ < n_qt ? k0 / BQ : n_qt) : 0;
+  const int per_head = n_qt - qt0;
+  const int n_work = p.group * per_head;
+  const int q_stride = (int)(p.q_sn * 2), o_stride = (int)(p.do_sn * 2);
+  const int q_dma_off = (int)dma_lane_offset<D, true>(lane, q_stride);
+  const int o_dma_off = (int)dma_lane_offset<D, true>(lane, o_stride);
+
+  auto issue = [&](int w, lds_char_t* qt, lds_char_t* ot, float* ls, float* dl) {
+    const int h = kvh * p.group + w / per_head;
+    const int q0 = (qt0 + w % per_head) * BQ;
+    const char* qbase = (const char*)p.q + (b * p.q_sb + h * p.q_sh) * 2;
+    const char* obase = (const char*)p.dout + (b * p.do_sb + h * p.do_sh) * 2;
+    dma_tile<D, BQ, NW>(qt, qbase, q_stride, q0, p.Nq, wave_u, q_dma_off);
+    dma_tile<D, BQ, NW>(ot, obase, o_stride, q0, p.Nq, wave_u, o_dma_off);
+    // logsumexp and Delta of the tile's rows: 4 bytes per lane, rows past Nq read as zero
+    const int64_t row0 = ((int64_t)b * p.Hq + h) * p.Nq + q0;
+    const int valid = p.Nq - q0 < BQ ? p.Nq - q0 : BQ;
+#pragma unroll
+    for (int part = 0; part < BQ / 64; ++part) {
+      if (wave_u == (2 * part) % NW) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.lse + row0 + 64 * part), (short)0, (int)(4 * (valid - 64 * part > 0 ? valid - 64 * part : 0)),
+            0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(ls + 64 * part), 4, 4 * lane, 0, 0, 0);
+      }
+      if (wave_u == (2 * part + 1) % NW) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.delta + row0 + 64 * part), (short)0,
+            (int)(4 * (valid - 64 * part > 0 ? valid - 64 * part : 0)), 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dl + 64 * part), 4, 4 * lane, 0, 0, 0);
+      }
+    }
+  };
+
+  const float c = p.c;
+  auto step = [&](auto stage_c, int w) {
+    constexpr int S = decltype(stage_c)::value;
+    lds_char_t* const qt = (lds_char_t*)(S == 0 ? q_st0_raw : q_st1_raw);
+    lds_char_t* const ot = (lds_char_t*)(S == 0 ? o_st0_raw : o_st1_raw);
+    const float* const ls = S == 0 ? ls_st0 : ls_st1;
+    const float* const dl = S == 0 ? dl_st0 : dl_st1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (w + 1 < n_work) {
+      if (S == 0)
+        issue(w + 1, (lds_char_t*)q_st1_raw, (lds_char_t*)o_st1_raw, ls_st1, dl_st1);
+      else
+        issue(w + 1, (lds_char_t*)q_st0_raw, (lds_char_t*)o_st0_raw, ls_st0, dl_st0);
+    }
+    const int q0 = (qt0 + w % per_head) * BQ;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qrow0 = q0 + 32 * qb;
+      // every query row of the block is before the wave's first key: nothing visible
+      if (CAUSAL && qrow0 + 31 < kw0) continue;
+      if (qrow0 >= p.Nq) continue;
+      f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int off = tile_chunk_offset<D, BQ, true>(32 * qb + (lane & 31), 2 * s + (lane >> 5));
+        const vec8 qa = __builtin_bit_cast(vec8, lds_read16(qt + off));
+        const vec8 oa = __builtin_bit_cast(vec8, lds_read16(ot + off));
+        s_acc = Elem<T>::mfma(qa, kf[s], s_acc);
+        dp_acc = Elem<T>::mfma(oa, vf[s], dp_acc);
+      }
+      // register r holds query row qrow0 + acc_row(r, lane) against the lane's key
+      vec8 pf[2], sf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = acc_row(r, lane);
+        const float lse2 = ls[32 * qb + m] * kLog2e;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c, -lse2));
+        if (CAUSAL && my_key > qrow0 + m) pv = 0.f;
+        const float ds = pv * (dp_acc[r] - dl[32 * qb + m]);
+        pf[r >> 3][r & 7] = (T)pv;
+        sf[r >> 3][r & 7] = (T)ds;
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 query rows (two 16-row slices)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int voff = vtr_lane_offset<D, BQ>(lane);
+          i16x4 olo = lds_read_tr(ot + voff + vtr_const_offset<D, BQ>(2 * qb + ks, 0, db));
+          i16x4 ohi = lds_read_tr(ot + voff + vtr_const_offset<D, BQ>(2 * qb + ks, 1, db));
+          i16x4 qlo = lds_read_tr(qt + voff + vtr_const_offset<D, BQ>(2 * qb + ks, 0, db));
+          i16x4 qhi = lds_read_tr(qt + voff + vtr_const_offset<D, BQ>(2 * qb + ks, 1, db));
+          if (DPAD && ((lane >> 4) & 1)) {
+            olo = i16x4{};
+            ohi = i16x4{};
+            qlo = i16x4{};
+            qhi = i16x4{};
+          }
+          const vec8 oT = __builtin_bit_cast(vec8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
+          const vec8 qT = __builtin_bit_cast(vec8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+          dvT[db] = Elem<T>::mfma(oT, pf[ks], dvT[db]);
+          dkT[db] = Elem<T>::mfma(qT, sf[ks], dkT[db]);
+        }
+    }
+  };
+
+  if (n_work > 0) issue(0, (lds_char_t*)q_st0_raw, (lds_char_t*)o_st0_raw, ls_st0, dl_st0);
+  int w = 0;
+  for (; w + 1 < n_work; w += 2) {
+    step(IC<0>(), w);
+    step(IC<1>(), w + 1);
+  }
+  if (w < n_work) step(IC<0>(), w);
+
+  // ---- epilogue: lane owns key my_key; register r of block db is head-dim 32*db + acc_row(r)
+  if (my_key < p.Nkv) {
+    char* dkrow = (char*)p.dk + (b * p.dk_sb + kvh * p.dk_sh + (int64_t)my_key * p.dk_sn) * 2;
+    char* dvrow = (char*)p.dv + (b * p.dv_sb + kvh * p.dv_sh + (int64_t)my_key * p.dv_sn) * 2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < (DPAD ? D / 8 : 4); ++g4) {
+        typename Elem<T>::vec4 kv, vv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv[e] = (T)(dkT[db][4 * g4 + e] * p.scale);
+          vv[e] = (T)dvT[db][4 * g4 + e];
+        }
+        const int col = 32 * db + acc_row(4 * g4, lane);
+        *(i32x2*)(dkrow + col * 2) = __builtin_bit_cast(i32x2, kv);
+        *(i32x2*)(dvrow + col * 2) = __builtin_bit_cast(i32x2, vv);
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// dQ. Grid: (ceil(Nq / BW), Hq, B).
+template <typename T, bool CAUSAL, class Cfg>
+__global__ void __launch_bounds__(Cfg::THREADS)
+    __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
+    fa_bwd_dq_kernel(const BwdParams p) {
+  constexpr int D = Cfg::D, NW = Cfg::NW, BKV = Cfg::BT, BQ = Cfg::BW;
+  constexpr int NS = D / 16;
+  constexpr bool DPAD = D < 32;
+  constexpr int NDB = DPAD ? 1 : D / 32;
+  constexpr int NKB = BKV / 32;
+  constexpr int NKS = BKV / 16;
+  constexpr int TB = Cfg::TILE_BYTES;
+  typedef typename Elem<T>::vec8 vec8;
+
+  // K in the transposing layout (row fragments for S^T, transposed for dQ^T), V in the row layout.
+  __shared__ __attribute__((aligned(1024))) char k_st0_raw[TB];
+  __shared__ __attribute__((aligned(1024))) char k_st1_raw[TB];
+  __shared__ __attribute__((aligned(1024))) char v_st0_raw[TB];
+  __shared__ __attribute__((aligned(1024))) char v_st1_raw[TB];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int kvh = h / p.group;
+  const int q0 = blockIdx.x * BQ;
+  const int wq0 = q0 + 32 * wave;
+  const int my_row = wq0 + (lane & 31);
+  const bool row_ok = my_row < p.Nq;
+
+  // Q and dO rows of the wave as B operands (lane holds row lane % 32); rows past Nq are zero.
+  vec8 qf[NS], of[NS];
+  {
+    const T* qrow = (const T*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)my_row * p.q_sn;
+    const T* orow = (const T*)p.dout + b * p.do_sb + h * p.do_sh + (int64_t)my_row * p.do_sn;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int col = 16 * s + 8 * half;
+      qf[s] = row_ok ? *(const vec8*)(qrow + col) : vec8{};
+      of[s] = row_ok ? *(const vec8*)(orow + col) : vec8{};
+    }
+  }
+  const int64_t stat = ((int64_t)b * p.Hq + h) * p.Nq + my_row;
+  const float lse2 = row_ok ? p.lse[stat] * kLog2e : 0.f;
+  const float dlt = row_ok ? p.delta[stat] : 0.f;
+  f32x16 dqT[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dqT[db] = f32x16{};
+
+  const char* kbase = (const char*)p.k + (b * p.k_sb + kvh * p.k_sh) * 2;
+  const char* vbase = (const char*)p.v + (b * p.v_sb + kvh * p.v_sh) * 2;
+  const int k_stride = (int)(p.k_sn * 2), v_stride = (int)(p.v_sn * 2);
+  const int k_dma_off = (int)dma_lane_offset<D, true>(lane, k_stride);
+  const int v_dma_off = (int)dma_lane_offset<D, false>(lane, v_stride);
+  const int n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
+  const int wq_last = wq0 + 31;
+  const float c = p.c;
+
+  constexpr int KP = kfrag_parities<D>();
+  int v_lane[KP];
+#pragma unroll
+  for (int par = 0; par < KP; ++par) v_lane[par] = kfrag_lane_offset<D, BKV>(par, lane);
+  const int kt_lane = vtr_lane_offset<D, BKV>(lane);
+
+  auto step = [&](auto stage_c, int j) {
+    constexpr int S = decltype(stage_c)::value;
+    lds_char_t* const kt = (lds_char_t*)(S == 0 ? k_st0_raw : k_st1_raw);
+    lds_char_t* const vt = (lds_char_t*)(S == 0 ? v_st0_raw : v_st1_raw);
+    const int kpos = j * BKV;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 < n_tiles) {
+      lds_char_t* const kn = (lds_char_t*)(S == 0 ? k_st1_raw : k_st0_raw);
+      lds_char_t* const vn = (lds_char_t*)(S == 0 ? v_st1_raw : v_st0_raw);
+      dma_tile<D, BKV, NW>(kn, kbase, k_stride, kpos + BKV, p.Nkv, wave_u, k_dma_off);
+      dma_tile<D, BKV, NW>(vn, vbase, v_stride, kpos + BKV, p.Nkv, wave_u, v_dma_off);
+    }
+    if (CAUSAL && kpos > wq_last) return;
+    f32x16 st[NKB], dpt[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      st[kb] = f32x16{};
+      dpt[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const vec8 ka = __builtin_bit_cast(
+            vec8, lds_read16(kt + tile_chunk_offset<D, BKV, true>(32 * kb + (lane & 31), 2 * s + half)));
+        const vec8 va =
+            __builtin_bit_cast(vec8, lds_read16(vt + v_lane[s % KP] + kfrag_const_offset<D, BKV>(kb, s)));
+        st[kb] = Elem<T>::mfma(ka, qf[s], st[kb]);
+        dpt[kb] = Elem<T>::mfma(va, of[s], dpt[kb]);
+      }
+    // register r of block kb: key kpos + 32*kb + acc_row(r, lane) against the lane's row
+    const int base = kpos + 4 * half;
+    int limit = p.Nkv - 1 - base;
+    if (CAUSAL) limit = min(limit, my_row - base);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int koff = 32 * kb + 8 * (r >> 2) + (r & 3);
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c, -lse2));
+        pv = koff > limit ? 0.f : pv;
+        st[kb][r] = pv * (dpt[kb][r] - dlt);  // dS^T / scale
+      }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      vec8 sfr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sfr[e] = (T)st[ks >> 1][pv_src_reg(ks, e)];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        i16x4 lo = lds_read_tr(kt + kt_lane + vtr_const_offset<D, BKV>(ks, 0, db));
+        i16x4 hi = lds_read_tr(kt + kt_lane + vtr_const_offset<D, BKV>(ks, 1, db));
+        if (DPAD && ((lane >> 4) & 1)) {
+          lo = i16x4{};
+          hi = i16x4{};
+        }
+        const vec8 kT = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dqT[db] = Elem<T>::mfma(kT, sfr, dqT[db]);
+      }
+    }
+  };
+
+  dma_tile<D, BKV, NW>((lds_char_t*)k_st0_raw, kbase, k_stride, 0, p.Nkv, wave_u, k_dma_off);
+  dma_tile<D, BKV, NW>((lds_char_t*)v_st0_raw, vbase, v_stride, 0, p.Nkv, wave_u, v_dma_off);
+  int j = 0;
+  for (; j + 1 < n_tiles; j += 2) {
+    step(IC<0>(), j);
+    step(IC<1>(), j + 1);
+  }
+  if (j < n_tiles) step(IC<0>(), j);
+
+  // ---- epilogue: dQ = scale * (dS K), lane owns row my_row; register r of block db is
+  // head-dim 32*db + acc_row(r)
+  if (row_ok) {
+    char* drow = (char*)p.dq + (b * p.dq_sb + h * p.dq_sh + (int64_t)my_row * p.dq_sn) * 2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < (DPAD ? D / 8 : 4); ++g4) {
+        typename Elem<T>::vec4 qv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[e] = (T)(dqT[db][4 * g4 + e] * p.scale);
+        const int col = 32 * db + acc_row(4 * g4, lane);
+        *(i32x2*)(drow + col * 2) = __builtin_bit_cast(i32x2, qv);
+      }
+  }
+}
+
+}  // namespace fa

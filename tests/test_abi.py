@@ -144,3 +144,40 @@ def test_product_path_has_no_cpu_fallback():
     from scaled_dot_product_fa2_amd import _binding
     with pytest.raises(RuntimeError):
         _binding.load_library("/nonexistent/libfa.so")
+
+
+BWD_VALID = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=0x50000, do=0x60000, dq=0x70000, dk=0x80000,
+                 dv=0x90000, delta=0xA0000, B=1, Hq=2, Hkv=1, Nq=128, Nkv=128, D=64,
+                 qs=(16384, 8192, 64, 1), ks=(8192, 8192, 64, 1), vs=(8192, 8192, 64, 1), os=(16384, 8192, 64, 1),
+                 dos=(16384, 8192, 64, 1), dqs=(16384, 8192, 64, 1), dks=(8192, 8192, 64, 1),
+                 dvs=(8192, 8192, 64, 1), scale=0.125, causal=1, dtype=1)
+
+
+def _bwd_call(**over):
+    a = dict(BWD_VALID)
+    a.update(over)
+    lib = _lib()
+    st = [(_st(*a[n]) if a[n] else None) for n in ("qs", "ks", "vs", "os", "dos", "dqs", "dks", "dvs")]
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["delta"],
+                      a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["D"], *st, a["scale"], a["causal"],
+                      a["dtype"], None)
+
+
+BWD_BAD = [
+    ("null_do", dict(do=0), "FA_ERR_NULL"), ("null_delta", dict(delta=0), "FA_ERR_NULL"),
+    ("null_dk", dict(dk=0), "FA_ERR_NULL"), ("null_do_stride", dict(dos=None), "FA_ERR_NULL"),
+    ("dtype", dict(dtype=3), "FA_ERR_DTYPE"), ("head_dim", dict(D=96), "FA_ERR_HEAD_DIM"),
+    ("gqa", dict(Hq=3, Hkv=2), "FA_ERR_GQA"), ("zero_nkv", dict(Nkv=0), "FA_ERR_SHAPE"),
+    ("batch_over_grid", dict(B=70000, qs=(0, 8192, 64, 1), ks=(0, 8192, 64, 1), vs=(0, 8192, 64, 1),
+                              os=(0, 8192, 64, 1), dos=(0, 8192, 64, 1)), "FA_ERR_SHAPE"),
+    ("dq_d_stride", dict(dqs=(16384, 8192, 64, 2)), "FA_ERR_LAYOUT"),
+    ("dk_zero_stride", dict(dks=(8192, 8192, 0, 1)), "FA_ERR_LAYOUT"),
+    ("misaligned_dv", dict(dv=0x90008), "FA_ERR_LAYOUT"), ("misaligned_delta", dict(delta=0xA0002), "FA_ERR_LAYOUT"),
+    ("do_odd_stride", dict(dos=(16384, 8192, 60, 1)), "FA_ERR_LAYOUT"),
+    ("scale_nan", dict(scale=float("nan")), "FA_ERR_SCALE"),
+]
+
+
+@pytest.mark.parametrize("name,over,code", BWD_BAD, ids=[b[0] for b in BWD_BAD])
+def test_bwd_validation_rejects(name, over, code):
+    assert _bwd_call(**over) == D_[code]
