@@ -123,12 +123,18 @@ int launch_d(int64_t D, const FwdParams& p, int64_t grid, hipStream_t stream) {
 }
 
 // ---- backward: per head dim, the dK/dV kernel (32 keys per wave, 64-row query tiles) and the
-// dQ kernel (32 query rows per wave, 64-key tiles; 32 at D = 256). D <= 64 fits two waves per SIMD.
+// dQ kernel (32 query rows per wave, 64-key tiles; 32 at D = 256). SPLIT_KV runs dV and dK as two
+// launches (S recomputed in each) so the registers of a wave hold one accumulator set, not two.
+#ifndef BWD_SPLIT_MIN_D
+#define BWD_SPLIT_MIN_D 256
+#endif
 template <int D>
 struct BwdCfgFor {
-  static constexpr int W = D <= 64 ? 2 : 1;
-  typedef fa::BwdCfg<D, 4, 64, W> dkdv;
-  typedef fa::BwdCfg<D, 4, D >= 256 ? 32 : 64, W> dq;
+  static constexpr bool SPLIT_KV = D >= BWD_SPLIT_MIN_D;
+  static constexpr int W_KV = D <= 64 ? 2 : (SPLIT_KV && D <= 128 ? 2 : 1);
+  static constexpr int W_Q = D <= 64 ? 2 : 1;
+  typedef fa::BwdCfg<D, 4, 64, W_KV> dkdv;
+  typedef fa::BwdCfg<D, 4, D >= 256 ? 32 : 64, W_Q> dq;
 };
 
 constexpr int64_t kMaxGridYZ = 65535;
@@ -142,9 +148,17 @@ int launch_bwd(const fa::BwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((fa::fa_bwd_delta_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                      stream, p);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK>),
-                     dim3((unsigned)((p.Nkv + CK::BW - 1) / CK::BW), (unsigned)p.Hkv, (unsigned)p.B),
-                     dim3(CK::THREADS), 0, stream, p);
+  const dim3 kv_grid((unsigned)((p.Nkv + CK::BW - 1) / CK::BW), (unsigned)p.Hkv, (unsigned)p.B);
+  if constexpr (BwdCfgFor<D>::SPLIT_KV) {
+    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyV>), kv_grid, dim3(CK::THREADS), 0,
+                       stream, p);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyK>), kv_grid, dim3(CK::THREADS), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdBoth>), kv_grid, dim3(CK::THREADS), 0,
+                       stream, p);
+  }
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<T, CAUSAL, CQ>),
                      dim3((unsigned)((p.Nq + CQ::BW - 1) / CQ::BW), (unsigned)p.Hq, (unsigned)p.B),

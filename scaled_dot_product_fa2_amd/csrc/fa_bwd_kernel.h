@@ -61,6 +61,16 @@ struct BwdParams {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// Fragment read-ahead of the gradient kernels, in fragments (as in the forward's loops).
+constexpr int kBwdLead = 3;
+
+// Compile-time part of the row-fragment read of rows 32*qb + (lane % 32), chunk 2*s + lane/32, of a
+// tile in the transposing (unswizzled) layout; the per-lane part depends on s only through its parity.
+template <int D, int ROWS>
+FA_HD int q_const(int qb, int s) {
+  return (2 * s / chunks_per_seg<D>()) * (ROWS * seg_bytes<D>()) + 32 * qb * seg_bytes<D>();
+}
+
 // Delta_i = sum_d O_id * dO_id for every (batch, head, row), fp32. D/8 lanes per row, one
 // 16-byte vector of O and of dO per lane, then a butterfly sum over those lanes.
 template <typename T, int D>
@@ -102,12 +112,16 @@ struct BwdCfg {
 };
 
 // ------------------------------------------------------------------------------------------------
-// dK, dV. Grid: (ceil(Nkv / BW), Hkv, B).
-template <typename T, bool CAUSAL, class Cfg>
+// dK, dV. Grid: (ceil(Nkv / BW), Hkv, B). PART selects the outputs: kBwdBoth, or one of
+// kBwdOnlyV / kBwdOnlyK (two launches, S recomputed in each, to fit wide heads in registers).
+constexpr int kBwdBoth = 0, kBwdOnlyV = 1, kBwdOnlyK = 2;
+
+template <typename T, bool CAUSAL, class Cfg, int PART>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
     fa_bwd_dkdv_kernel(const BwdParams p) {
   constexpr int D = Cfg::D, NW = Cfg::NW, BQ = Cfg::BT, BK = Cfg::BW;
+  constexpr bool DO_V = PART != kBwdOnlyK, DO_K = PART != kBwdOnlyV;
   constexpr int NS = D / 16;
   constexpr bool DPAD = D < 32;
   constexpr int NDB = DPAD ? 1 : D / 32;
@@ -145,7 +159,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     for (int s = 0; s < NS; ++s) {
       const int col = 16 * s + 8 * (lane >> 5);
       kf[s] = my_key < p.Nkv ? *(const vec8*)(krow + col) : vec8{};
-      vf[s] = my_key < p.Nkv ? *(const vec8*)(vrow + col) : vec8{};
+      if (DO_K) vf[s] = my_key < p.Nkv ? *(const vec8*)(vrow + col) : vec8{};
     }
   }
   f32x16 dkT[NDB], dvT[NDB];
@@ -191,6 +205,13 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     }
   };
 
+  // per-lane parts of the tile reads: row fragments of the Q/dO tiles (transposing layout, so the
+  // chunk slot is not swizzled) and the transposing reads
+  constexpr int KP = kfrag_parities<D>();
+  int q_lane[KP];
+#pragma unroll
+  for (int par = 0; par < KP; ++par) q_lane[par] = tile_chunk_offset<D, BQ, true>(lane & 31, 2 * par + (lane >> 5));
+  const int t_lane = vtr_lane_offset<D, BQ>(lane);
   const float c = p.c;
   auto step = [&](auto stage_c, int w) {
     constexpr int S = decltype(stage_c)::value;
@@ -214,47 +235,89 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       if (CAUSAL && qrow0 + 31 < kw0) continue;
       if (qrow0 >= p.Nq) continue;
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+      {
+        vec8 qa[NS], oa[NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int off = tile_chunk_offset<D, BQ, true>(32 * qb + (lane & 31), 2 * s + (lane >> 5));
-        const vec8 qa = __builtin_bit_cast(vec8, lds_read16(qt + off));
-        const vec8 oa = __builtin_bit_cast(vec8, lds_read16(ot + off));
-        s_acc = Elem<T>::mfma(qa, kf[s], s_acc);
-        dp_acc = Elem<T>::mfma(oa, vf[s], dp_acc);
+        for (int s = 0; s < NS; ++s) {
+          const int off = q_lane[s % KP] + q_const<D, BQ>(qb, s);
+          qa[s] = __builtin_bit_cast(vec8, lds_read16(qt + off));
+          if (DO_K) oa[s] = __builtin_bit_cast(vec8, lds_read16(ot + off));
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          s_acc = Elem<T>::mfma(qa[s], kf[s], s_acc);
+          if (DO_K) dp_acc = Elem<T>::mfma(oa[s], vf[s], dp_acc);
+        }
+        constexpr int PER = DO_K ? 2 : 1;
+        constexpr int LEAD = kBwdLead < NS ? kBwdLead : NS;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PER * LEAD, 0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, PER, 0);
+          if (s + LEAD < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PER, 0);
+        }
       }
-      // register r holds query row qrow0 + acc_row(r, lane) against the lane's key
+      // register r holds query row qrow0 + acc_row(r, lane) against the lane's key; registers
+      // 4g .. 4g+3 are four consecutive rows, so their logsumexp and Delta are one 16-byte read
       vec8 pf[2], sf[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = acc_row(r, lane);
-        const float lse2 = ls[32 * qb + m] * kLog2e;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c, -lse2));
-        if (CAUSAL && my_key > qrow0 + m) pv = 0.f;
-        const float ds = pv * (dp_acc[r] - dl[32 * qb + m]);
-        pf[r >> 3][r & 7] = (T)pv;
-        sf[r >> 3][r & 7] = (T)ds;
+      for (int g = 0; g < 4; ++g) {
+        const int m0 = 8 * g + 4 * (lane >> 5);
+        const float4 l4 = *(const float4*)(ls + 32 * qb + m0);
+        const float4 d4 = DO_K ? *(const float4*)(dl + 32 * qb + m0) : float4{};
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c, -lv[e] * kLog2e));
+          if (CAUSAL && my_key > qrow0 + m0 + e) pv = 0.f;
+          const float ds = pv * (dp_acc[r] - dv4[e]);
+          pf[r >> 3][r & 7] = (T)pv;
+          sf[r >> 3][r & 7] = (T)ds;
+        }
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 query rows (two 16-row slices)
+      {
+        vec8 oT[2][NDB], qT[2][NDB];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int voff = vtr_lane_offset<D, BQ>(lane);
-          i16x4 olo = lds_read_tr(ot + voff + vtr_const_offset<D, BQ>(2 * qb + ks, 0, db));
-          i16x4 ohi = lds_read_tr(ot + voff + vtr_const_offset<D, BQ>(2 * qb + ks, 1, db));
-          i16x4 qlo = lds_read_tr(qt + voff + vtr_const_offset<D, BQ>(2 * qb + ks, 0, db));
-          i16x4 qhi = lds_read_tr(qt + voff + vtr_const_offset<D, BQ>(2 * qb + ks, 1, db));
-          if (DPAD && ((lane >> 4) & 1)) {
-            olo = i16x4{};
-            ohi = i16x4{};
-            qlo = i16x4{};
-            qhi = i16x4{};
+          for (int db = 0; db < NDB; ++db) {
+            i16x4 olo{}, ohi{}, qlo{}, qhi{};
+            if (DO_V) {
+              olo = lds_read_tr(ot + t_lane + vtr_const_offset<D, BQ>(2 * qb + ks, 0, db));
+              ohi = lds_read_tr(ot + t_lane + vtr_const_offset<D, BQ>(2 * qb + ks, 1, db));
+            }
+            if (DO_K) {
+              qlo = lds_read_tr(qt + t_lane + vtr_const_offset<D, BQ>(2 * qb + ks, 0, db));
+              qhi = lds_read_tr(qt + t_lane + vtr_const_offset<D, BQ>(2 * qb + ks, 1, db));
+            }
+            if (DPAD && ((lane >> 4) & 1)) {
+              olo = i16x4{};
+              ohi = i16x4{};
+              qlo = i16x4{};
+              qhi = i16x4{};
+            }
+            oT[ks][db] = __builtin_bit_cast(vec8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
+            qT[ks][db] = __builtin_bit_cast(vec8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
           }
-          const vec8 oT = __builtin_bit_cast(vec8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
-          const vec8 qT = __builtin_bit_cast(vec8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
-          dvT[db] = Elem<T>::mfma(oT, pf[ks], dvT[db]);
-          dkT[db] = Elem<T>::mfma(qT, sf[ks], dkT[db]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            if (DO_V) dvT[db] = Elem<T>::mfma(oT[ks][db], pf[ks], dvT[db]);
+            if (DO_K) dkT[db] = Elem<T>::mfma(qT[ks][db], sf[ks], dkT[db]);
+          }
+        constexpr int PER = (DO_V ? 1 : 0) + (DO_K ? 1 : 0);
+        constexpr int NF = 2 * NDB;
+        constexpr int LEAD = kBwdLead < NF ? kBwdLead : NF;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PER * LEAD, 0);
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, PER, 0);
+          if (i + LEAD < NF) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PER, 0);
         }
+      }
     }
   };
 
@@ -281,8 +344,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           vv[e] = (T)dvT[db][4 * g4 + e];
         }
         const int col = 32 * db + acc_row(4 * g4, lane);
-        *(i32x2*)(dkrow + col * 2) = __builtin_bit_cast(i32x2, kv);
-        *(i32x2*)(dvrow + col * 2) = __builtin_bit_cast(i32x2, vv);
+        if (DO_K) *(i32x2*)(dkrow + col * 2) = __builtin_bit_cast(i32x2, kv);
+        if (DO_V) *(i32x2*)(dvrow + col * 2) = __builtin_bit_cast(i32x2, vv);
       }
   }
 }
@@ -349,9 +412,12 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const float c = p.c;
 
   constexpr int KP = kfrag_parities<D>();
-  int v_lane[KP];
+  int v_lane[KP], k_lane[KP];
 #pragma unroll
-  for (int par = 0; par < KP; ++par) v_lane[par] = kfrag_lane_offset<D, BKV>(par, lane);
+  for (int par = 0; par < KP; ++par) {
+    v_lane[par] = kfrag_lane_offset<D, BKV>(par, lane);
+    k_lane[par] = tile_chunk_offset<D, BKV, true>(lane & 31, 2 * par + half);
+  }
   const int kt_lane = vtr_lane_offset<D, BKV>(lane);
 
   auto step = [&](auto stage_c, int j) {
@@ -374,17 +440,30 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       st[kb] = f32x16{};
       dpt[kb] = f32x16{};
     }
+    {
+      vec8 ka[NS][NKB], va[NS][NKB];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const vec8 ka = __builtin_bit_cast(
-            vec8, lds_read16(kt + tile_chunk_offset<D, BKV, true>(32 * kb + (lane & 31), 2 * s + half)));
-        const vec8 va =
-            __builtin_bit_cast(vec8, lds_read16(vt + v_lane[s % KP] + kfrag_const_offset<D, BKV>(kb, s)));
-        st[kb] = Elem<T>::mfma(ka, qf[s], st[kb]);
-        dpt[kb] = Elem<T>::mfma(va, of[s], dpt[kb]);
+        for (int kb = 0; kb < NKB; ++kb) {
+          ka[s][kb] = __builtin_bit_cast(vec8, lds_read16(kt + k_lane[s % KP] + q_const<D, BKV>(kb, s)));
+          va[s][kb] = __builtin_bit_cast(vec8, lds_read16(vt + v_lane[s % KP] + kfrag_const_offset<D, BKV>(kb, s)));
+        }
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          st[kb] = Elem<T>::mfma(ka[s][kb], qf[s], st[kb]);
+          dpt[kb] = Elem<T>::mfma(va[s][kb], of[s], dpt[kb]);
+        }
+      constexpr int LEAD = kBwdLead < NS ? kBwdLead : NS;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * NKB * LEAD, 0);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * NKB, 0);
+        if (s + LEAD < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * NKB, 0);
       }
+    }
     // register r of block kb: key kpos + 32*kb + acc_row(r, lane) against the lane's row
     const int base = kpos + 4 * half;
     int limit = p.Nkv - 1 - base;
@@ -398,21 +477,36 @@ __global__ void __launch_bounds__(Cfg::THREADS)
         pv = koff > limit ? 0.f : pv;
         st[kb][r] = pv * (dpt[kb][r] - dlt);  // dS^T / scale
       }
+    vec8 sfr[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      vec8 sfr;
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sfr[e] = (T)st[ks >> 1][pv_src_reg(ks, e)];
+      for (int e = 0; e < 8; ++e) sfr[ks][e] = (T)st[ks >> 1][pv_src_reg(ks, e)];
+    {
+      vec8 kT[NKS][NDB];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        i16x4 lo = lds_read_tr(kt + kt_lane + vtr_const_offset<D, BKV>(ks, 0, db));
-        i16x4 hi = lds_read_tr(kt + kt_lane + vtr_const_offset<D, BKV>(ks, 1, db));
-        if (DPAD && ((lane >> 4) & 1)) {
-          lo = i16x4{};
-          hi = i16x4{};
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          i16x4 lo = lds_read_tr(kt + kt_lane + vtr_const_offset<D, BKV>(ks, 0, db));
+          i16x4 hi = lds_read_tr(kt + kt_lane + vtr_const_offset<D, BKV>(ks, 1, db));
+          if (DPAD && ((lane >> 4) & 1)) {
+            lo = i16x4{};
+            hi = i16x4{};
+          }
+          kT[ks][db] = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
-        const vec8 kT = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        dqT[db] = Elem<T>::mfma(kT, sfr, dqT[db]);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dqT[db] = Elem<T>::mfma(kT[ks][db], sfr[ks], dqT[db]);
+      constexpr int NF = NKS * NDB;
+      constexpr int LEAD = kBwdLead + 1 < NF ? kBwdLead + 1 : NF;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * LEAD, 0);
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (i + LEAD < NF) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
     }
   };
