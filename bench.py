@@ -7,6 +7,9 @@ seeded N(0,1) inputs already resident in HBM). FLOP per forward is
 4*B*Hq*Nq*Nkv*D, halved for the causal mask. `value` is total FLOP / total time.
 
 Prints ONE JSON line. Extra objects:
+  backward      - the backward (fa_bwd: Delta, dK/dV and dQ kernels) on the same inputs with a seeded
+                  N(0,1) dO, per mask: time per call from HIP events and TFLOP/s counting the five
+                  products of the backward (10*B*Hq*Nq*Nkv*D, halved for the causal mask).
   roofline      - the dominant launch (the non-causal forward): algorithmic FLOP / its average
                   duration from HIP events on the launch stream, against the dense bf16 MFMA peak;
                   `traffic` is the HBM bytes per launch from committed rocprofv3 counters when they
@@ -14,6 +17,7 @@ Prints ONE JSON line. Extra objects:
   cpu_baseline  - the float64 CPU oracle timed on this host's cores on the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                      [--no-backward]
 """
 from __future__ import annotations
 
@@ -94,6 +98,39 @@ def cpu_baseline(w, q, k, v, outs):
                                                           "lse_abs_err_max": worst_l}}
 
 
+def backward_timing(w, q, k, v, outs, modes, steps, stream):
+    """Time fa_bwd on the forward's own outputs, per mask, with HIP events on the launch stream."""
+    import torch
+    import scaled_dot_product_fa2_amd as fa
+    g = torch.Generator().manual_seed(w.seed + 17)
+    do = torch.randn(w.B, w.Hq, w.Nq, w.D, generator=g).to(w.dtype).to(q.device)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    delta = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=q.device)
+    res = {}
+    for c in modes:
+        o, lse = outs[c]
+
+        def call():
+            fa.fa_bwd(q, k, v, o, lse, do, causal=c, dq=grads[0], dk=grads[1], dv=grads[2], delta=delta,
+                      stream=stream)
+
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        f = 2.5 * flop(w, c)
+        res["causal" if c else "non_causal"] = {"ms_per_call": round(ms, 5), "tflops": round(f / (ms / 1e3) / 1e12, 2),
+                                                "frac_of_peak": round(f / (ms / 1e3) / 1e12 / PEAK_TFLOPS[w.dtype_name], 4),
+                                                "calls": steps}
+    return {"metric": "attention bwd TFLOP/s (five products: 10*B*Hq*Nq*Nkv*D, halved for causal)", "per_mode": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +138,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="b4h16n1024d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB, 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -193,6 +231,8 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "kernel_sha": kernel_sha(),
     }
+    if not args.no_backward:
+        result["backward"] = backward_timing(w, qd, kd, vd, outs, modes, max(5, min(args.steps, 50)), stream)
     if not args.no_cpu_baseline:
         outs_cpu = {c: (outs[c][0].cpu(), outs[c][1].cpu()) for c in modes}
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, outs_cpu)
