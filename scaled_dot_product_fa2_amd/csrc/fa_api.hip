@@ -125,14 +125,18 @@ int launch_d(int64_t D, const FwdParams& p, int64_t grid, hipStream_t stream) {
 // ---- backward: per head dim, the dK/dV kernel (32 keys per wave, 64-row query tiles) and the
 // dQ kernel (32 query rows per wave, 64-key tiles; 32 at D = 256). SPLIT_KV runs dV and dK as two
 // launches (S recomputed in each) so the registers of a wave hold one accumulator set, not two.
+// Waves per SIMD: dK/dV two up to D = 64, dQ two up to D = 128, otherwise one (register limits).
 #ifndef BWD_SPLIT_MIN_D
 #define BWD_SPLIT_MIN_D 256
+#endif
+#ifndef BWD_DQ_W2_MAX_D
+#define BWD_DQ_W2_MAX_D 128
 #endif
 template <int D>
 struct BwdCfgFor {
   static constexpr bool SPLIT_KV = D >= BWD_SPLIT_MIN_D;
   static constexpr int W_KV = D <= 64 ? 2 : (SPLIT_KV && D <= 128 ? 2 : 1);
-  static constexpr int W_Q = D <= 64 ? 2 : 1;
+  static constexpr int W_Q = D <= BWD_DQ_W2_MAX_D ? 2 : 1;
   typedef fa::BwdCfg<D, 4, 64, W_KV> dkdv;
   typedef fa::BwdCfg<D, 4, D >= 256 ? 32 : 64, W_Q> dq;
 };

@@ -62,7 +62,10 @@ struct BwdParams {
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // Fragment read-ahead of the gradient kernels, in fragments (as in the forward's loops).
-constexpr int kBwdLead = 3;
+#ifndef BWD_LEAD
+#define BWD_LEAD 3
+#endif
+constexpr int kBwdLead = BWD_LEAD;
 
 // Compile-time part of the row-fragment read of rows 32*qb + (lane % 32), chunk 2*s + lane/32, of a
 // tile in the transposing (unswizzled) layout; the per-lane part depends on s only through its parity.
