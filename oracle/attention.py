@@ -24,6 +24,12 @@ emulated here:
 * grouped-query heads: query head h reads key/value head h // (Hq / Hkv)
   ("Write Triton Attention Kernel", step 1 and Kernel design rules).
 
+A sliding window ("Write Triton Attention Kernel", Inputs item 3, which lists
+sliding-window masks beside the causal one) restricts row i to keys
+i - left <= j <= i + right (either side may be unbounded); the causal mask is
+the window (unbounded, 0). A row whose visible key set is empty (possible only
+with a window) has no softmax; the oracle returns o = 0 and lse = -inf for it.
+
 Readings where the pages leave a point open: the causal mask is top-left even
 when Nq != Nkv; a row whose key set is empty cannot occur under that reading
 (key 0 is always visible), and empty key sets (Nkv = 0) are rejected; the
@@ -71,10 +77,12 @@ def _check_shapes(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> Tuple[int, int
 
 
 def head_ref(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: np.ndarray, *, causal: bool,
-             scale: float, row_chunk: int = 512) -> Tuple[np.ndarray, np.ndarray]:
+             scale: float, row_chunk: int = 512,
+             window: Optional[Tuple[Optional[int], Optional[int]]] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Attention of the selected query rows of one head against one key/value head.
 
     qh: (Nq, D), kh: (Nkv, D), vh: (Nkv, Dv), rows: integer query positions.
+    window: optional (left, right); row i then sees keys i - left .. i + right (None = unbounded).
     Returns (o, lse) with shapes (len(rows), Dv) and (len(rows),), float64.
     """
     qh, kh, vh = _f64(qh), _f64(kh), _f64(vh)
@@ -89,20 +97,31 @@ def head_ref(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: np.ndarray, *
         if causal:
             visible = key_pos[None, :] <= r[:, None]     # top-left causal: key j visible to row i iff j <= i
             s = np.where(visible, s, -np.inf)
+        if window is not None:
+            left, right = window
+            if left is not None:
+                s = np.where(key_pos[None, :] >= r[:, None] - left, s, -np.inf)   # j >= i - left
+            if right is not None:
+                s = np.where(key_pos[None, :] <= r[:, None] + right, s, -np.inf)  # j <= i + right
+        empty = np.all(s == -np.inf, axis=1)             # only a window can leave a row without keys
+        s[empty] = 0.0
         m = np.max(s, axis=1, keepdims=True)             # row maximum over the visible keys
         e = np.exp(s - m)                                # masked entries give exp(-inf) = 0
+        e[empty] = 0.0
         l = np.sum(e, axis=1, keepdims=True)             # softmax denominator
+        l[empty] = 1.0
         o[start:start + r.shape[0]] = (e / l) @ vh       # softmax-weighted sum of value rows
-        lse[start:start + r.shape[0]] = m[:, 0] + np.log(l[:, 0])
+        lse[start:start + r.shape[0]] = np.where(empty, -np.inf, m[:, 0] + np.log(l[:, 0]))
     return o, lse
 
 
 def attention_ref(q, k, v, *, causal: bool, scale: Optional[float] = None,
-                  row_chunk: int = 512) -> Tuple[np.ndarray, np.ndarray]:
+                  row_chunk: int = 512, window=None) -> Tuple[np.ndarray, np.ndarray]:
     """Full attention forward in float64.
 
     q: (B, Hq, Nq, D); k: (B, Hkv, Nkv, D); v: (B, Hkv, Nkv, Dv); any float dtype,
-    any strides. ``scale`` defaults to 1/sqrt(D). Returns o (B, Hq, Nq, Dv) and
+    any strides. ``scale`` defaults to 1/sqrt(D); ``window`` is an optional (left, right)
+    sliding window (None on a side = unbounded). Returns o (B, Hq, Nq, Dv) and
     lse (B, Hq, Nq), both float64.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -117,12 +136,12 @@ def attention_ref(q, k, v, *, causal: bool, scale: Optional[float] = None,
         for h in range(Hq):
             kvh = h // group
             o[b, h], lse[b, h] = head_ref(q[b, h], k[b, kvh], v[b, kvh], rows, causal=causal,
-                                          scale=scale, row_chunk=row_chunk)
+                                          scale=scale, row_chunk=row_chunk, window=window)
     return o, lse
 
 
 def attention_rows(q, k, v, b: int, h: int, rows: Sequence[int], *, causal: bool,
-                   scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+                   scale: Optional[float] = None, window=None) -> Tuple[np.ndarray, np.ndarray]:
     """Attention for selected query rows of (batch b, query head h) only.
 
     Used to check sampled outputs of shapes too large to compute in full.
@@ -136,7 +155,7 @@ def attention_rows(q, k, v, b: int, h: int, rows: Sequence[int], *, causal: bool
         scale = 1.0 / math.sqrt(D)
     kvh = h // (Hq // Hkv)
     return head_ref(_f64(q[b, h]), _f64(k[b, kvh]), _f64(v[b, kvh]), np.asarray(rows), causal=causal,
-                    scale=scale)
+                    scale=scale, window=window)
 
 
 # ---------------------------------------------------------------------------------------------

@@ -361,9 +361,109 @@ def pin_large_scores(mod):
     _close(lse[0, 0, 2], math.log(3.0), what="large scores, negative row lse")
 
 
+# ---------------------------------------------------------------------------------------------
+# Sliding windows: row i sees keys i - left .. i + right (None = unbounded on that side).
+
+def _brute_window(q, k, v, left, right, scale):
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, Nq, Dv))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for i in range(Nq):
+                keys = [j for j in range(Nkv) if (left is None or j >= i - left) and (right is None or j <= i + right)]
+                if not keys:
+                    continue
+                s = {j: scale * math.fsum(float(q[b, h, i, d]) * float(k[b, g, j, d]) for d in range(D)) for j in keys}
+                z = math.log(math.fsum(math.exp(s[j]) for j in keys))
+                lse[b, h, i] = z
+                for e in range(Dv):
+                    o[b, h, i, e] = math.fsum(math.exp(s[j] - z) * float(v[b, g, j, e]) for j in keys)
+    return o, lse
+
+
+def _close_lse(a, b, what):
+    a, b = np.asarray(a), np.asarray(b)
+    assert np.array_equal(np.isneginf(a), np.isneginf(b)), f"{what}: -inf pattern differs"
+    fin = ~np.isneginf(b)
+    _close(a[fin], b[fin], what=what)
+
+
+def pin_window_brute_force(mod):
+    rng = _rng(31)
+    for Hq, Hkv in [(1, 1), (2, 1)]:
+        for Nq, Nkv in [(6, 6), (7, 4), (4, 9)]:
+            for left, right in [(0, 0), (1, 0), (2, 1), (None, 1), (1, None), (3, 2), (0, None)]:
+                q = _rand(rng, 1, Hq, Nq, 3)
+                k = _rand(rng, 1, Hkv, Nkv, 3)
+                v = _rand(rng, 1, Hkv, Nkv, 4)
+                o, lse = mod.attention_ref(q, k, v, causal=False, scale=0.8, window=(left, right))
+                ob, lb = _brute_window(q, k, v, left, right, 0.8)
+                what = f"window brute Hq={Hq} Nq={Nq} Nkv={Nkv} window=({left},{right})"
+                _close(o, ob, what=what + " o")
+                _close_lse(lse, lb, what=what + " lse")
+
+
+def pin_window_sdpa_bool_mask(mod):
+    """torch float64 SDPA with an explicit boolean band mask (windows that leave no row empty)."""
+    rng = _rng(32)
+    for Nq, Nkv, left, right in [(20, 20, 5, 0), (20, 20, 3, 4), (16, 30, 7, 7), (30, 16, None, 2)]:
+        q = _rand(rng, 1, 4, Nq, 8)
+        k = _rand(rng, 1, 2, Nkv, 8)
+        v = _rand(rng, 1, 2, Nkv, 8)
+        o, _ = mod.attention_ref(q, k, v, causal=False, scale=0.4, window=(left, right))
+        i = np.arange(Nq)[:, None]
+        j = np.arange(Nkv)[None, :]
+        band = np.ones((Nq, Nkv), dtype=bool)
+        if left is not None:
+            band &= j >= i - left
+        if right is not None:
+            band &= j <= i + right
+        assert band.any(axis=1).all()
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=torch.from_numpy(band),
+            scale=0.4, enable_gqa=True).numpy()
+        _close(o, ref, tol=1e-10, what=f"window sdpa ({left},{right})")
+
+
+def pin_window_special_cases(mod):
+    rng = _rng(33)
+    q = _rand(rng, 1, 2, 9, 4)
+    k = _rand(rng, 1, 2, 9, 4)
+    v = _rand(rng, 1, 2, 9, 5)
+    # (unbounded, 0) is the causal mask; (unbounded, unbounded) is no mask
+    oc, lc = mod.attention_ref(q, k, v, causal=True, scale=0.6)
+    ow, lw = mod.attention_ref(q, k, v, causal=False, scale=0.6, window=(None, 0))
+    _close(ow, oc, what="window (None, 0) o")
+    _close(lw, lc, what="window (None, 0) lse")
+    of, lf = mod.attention_ref(q, k, v, causal=False, scale=0.6)
+    ou, lu = mod.attention_ref(q, k, v, causal=False, scale=0.6, window=(None, None))
+    _close(ou, of, what="window (None, None) o")
+    _close(lu, lf, what="window (None, None) lse")
+    # (0, 0): each row sees only its own position, so o_i = v_i and lse_i = scale * q_i . k_i;
+    # rows past the last key see nothing: o = 0, lse = -inf
+    qq = _rand(rng, 1, 1, 7, 4)
+    kk = _rand(rng, 1, 1, 5, 4)
+    vv = _rand(rng, 1, 1, 5, 3)
+    o0, l0 = mod.attention_ref(qq, kk, vv, causal=False, scale=0.5, window=(0, 0))
+    _close(o0[0, 0, :5], vv[0, 0], what="window (0, 0) o")
+    _close(l0[0, 0, :5], 0.5 * np.sum(qq[0, 0, :5] * kk[0, 0], axis=1), what="window (0, 0) lse")
+    assert np.all(o0[0, 0, 5:] == 0.0) and np.all(np.isneginf(l0[0, 0, 5:])), "empty rows: o = 0, lse = -inf"
+    # the sampled-rows entry point agrees with the full computation under a window
+    rows = [0, 4, 8]
+    o_r, l_r = mod.attention_rows(q, k, v, 0, 1, rows, causal=False, scale=0.6, window=(2, 1))
+    o_a, l_a = mod.attention_ref(q, k, v, causal=False, scale=0.6, window=(2, 1))
+    _close(o_r, o_a[0, 1, rows], what="window rows o")
+    _close(l_r, l_a[0, 1, rows], what="window rows lse")
+
+
 ALL_PINS = [
     pin_brute_force, pin_sdpa_float64, pin_lse_scipy, pin_single_key, pin_zero_query,
     pin_first_causal_row, pin_default_scale, pin_scale_moves_to_q, pin_convex_rows, pin_affine_v,
     pin_key_shift, pin_gqa_is_repeated_mha, pin_causal_prefix, pin_key_permutation,
     pin_two_block_merge, pin_strided_views, pin_rows_agree, pin_large_scores,
+    pin_window_brute_force, pin_window_sdpa_bool_mask, pin_window_special_cases,
 ]

@@ -32,6 +32,10 @@ MUTANTS = [
     ("q_rows_shifted", "(qh[r] @ kh.T)", "(qh[(r + 1) % qh.shape[0]] @ kh.T)"),
     ("max_over_all_rows", "m = np.max(s, axis=1, keepdims=True)", "m = np.max(s, keepdims=True)"),
     ("denominator_offset", "l = np.sum(e, axis=1, keepdims=True)", "l = np.sum(e, axis=1, keepdims=True) + 1e-3"),
+    ("window_left_off_by_one", "r[:, None] - left, s", "r[:, None] - left + 1, s"),
+    ("window_right_ignored", "if right is not None:\n                s", "if False:\n                s"),
+    ("window_right_as_left", "r[:, None] + right, s", "r[:, None] + left, s"),
+    ("empty_row_lse_zero", "np.where(empty, -np.inf,", "np.where(empty, 0.0,"),
 ]
 
 
