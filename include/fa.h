@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 /* Element types of Q, K, V and O (all four share one type). */
 #define FA_DTYPE_F16 0
@@ -83,6 +83,24 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int64_t q_stride[4], const int64_t k_stride[4],
            const int64_t v_stride[4], const int64_t o_stride[4],
            float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_fwd_window - fa_fwd with a sliding-window mask in place of the causal flag: query row i
+ * sees the keys j with i - window_left <= j <= i + window_right (zero-based positions, the same
+ * top-left anchoring as the causal mask). window_left / window_right = -1 leaves that side
+ * unbounded, so (-1, 0) is the causal mask and (-1, -1) no mask. The sliding-window mask is
+ * one of the masking variants "Write Triton Attention Kernel" lists among its inputs (item 3).
+ * A row whose window holds no key (e.g. row i >= Nkv with window_left = 0) has no softmax:
+ * its O row is written as zeros and its LSE as -inf.
+ *
+ * Arguments, layout, ownership and errors as in fa_fwd; additionally window_left and
+ * window_right must be >= -1 and Nq, Nkv <= 2^30 (FA_ERR_SHAPE otherwise).
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                  const int64_t q_stride[4], const int64_t k_stride[4],
+                  const int64_t v_stride[4], const int64_t o_stride[4],
+                  float scale, int64_t window_left, int64_t window_right, int dtype, void* stream);
 
 /*
  * fa_bwd - enqueue the attention backward on `stream` and return: given the

@@ -45,6 +45,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p, f32, i32,
                            i32, vp]
     lib.fa_fwd.restype = i32
+    lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p, f32,
+                                  i64, i64, i32, vp]
+    lib.fa_fwd_window.restype = i32
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                            i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f32, i32, i32, vp]
     lib.fa_bwd.restype = i32
@@ -210,3 +213,38 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
         ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return dq, dk, dv
+
+
+def fa_fwd_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, window_left: int = -1,
+                  window_right: int = -1, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention forward with a sliding window: query row i sees keys i - window_left .. i + window_right
+    (-1 = unbounded on that side). Same tensors, rules and return values as ``fa_fwd``; a row whose
+    window holds no key gets O = 0 and LSE = -inf."""
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nkv, _ = k.shape
+    if k.shape != (B, Hkv, Nkv, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, D), dtype=q.dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must match q in shape, dtype and device")
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, Hq, Nq) tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    code = load_library().fa_fwd_window(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(out),
+        float(scale), int(window_left), int(window_right), _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return out, lse

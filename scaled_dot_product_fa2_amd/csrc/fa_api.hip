@@ -90,6 +90,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Largest sequence stride (elements): a tile of up to 256 rows is addressed with 32-bit offsets.
 constexpr int64_t kMaxRowStride = (int64_t)1 << 22;
 
+// Sequence lengths of a windowed forward: row + window stays within 32 bits.
+constexpr int64_t kMaxWindowSeq = (int64_t)1 << 30;
+
 int check_strides(const int64_t* st, bool is_output, int64_t B, int64_t H, int64_t N) {
   if (st[3] != 1) return FA_ERR_LAYOUT;
   for (int i = 0; i < 3; ++i) {
@@ -103,23 +106,67 @@ int check_strides(const int64_t* st, bool is_output, int64_t B, int64_t H, int64
   return FA_OK;
 }
 
-template <typename T, bool CAUSAL, int D>
+template <typename T, bool CAUSAL, int D, bool WINDOW = false>
 int launch(const FwdParams& p, int64_t grid, hipStream_t stream) {
   typedef typename CfgFor<D>::type C;
-  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, CAUSAL, C>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, CAUSAL, C, WINDOW>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
+                     p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, bool WINDOW = false>
 int launch_d(int64_t D, const FwdParams& p, int64_t grid, hipStream_t stream) {
   switch (D) {
-    case 16: return launch<T, CAUSAL, 16>(p, grid, stream);
-    case 32: return launch<T, CAUSAL, 32>(p, grid, stream);
-    case 64: return launch<T, CAUSAL, 64>(p, grid, stream);
-    case 128: return launch<T, CAUSAL, 128>(p, grid, stream);
-    case 256: return launch<T, CAUSAL, 256>(p, grid, stream);
+    case 16: return launch<T, CAUSAL, 16, WINDOW>(p, grid, stream);
+    case 32: return launch<T, CAUSAL, 32, WINDOW>(p, grid, stream);
+    case 64: return launch<T, CAUSAL, 64, WINDOW>(p, grid, stream);
+    case 128: return launch<T, CAUSAL, 128, WINDOW>(p, grid, stream);
+    case 256: return launch<T, CAUSAL, 256, WINDOW>(p, grid, stream);
     default: return FA_ERR_HEAD_DIM;
   }
+}
+
+// Shared validation and parameter setup of the forward entry points.
+int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                int64_t Nq, int64_t Nkv, int64_t D, const int64_t* q_stride, const int64_t* k_stride,
+                const int64_t* v_stride, const int64_t* o_stride, float scale, bool causal, int dtype, FwdParams* p,
+                int64_t* grid) {
+  if (!q || !k || !v || !o || !lse || !q_stride || !k_stride || !v_stride || !o_stride) return FA_ERR_NULL;
+  PlanInfo pi;
+  int64_t n_qt = 0;
+  int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, causal, &pi, &n_qt, grid);
+  if (rc != FA_OK) return rc;
+  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_SCALE;
+  if ((rc = check_strides(q_stride, false, B, Hq, Nq)) != FA_OK) return rc;
+  if ((rc = check_strides(k_stride, false, B, Hkv, Nkv)) != FA_OK) return rc;
+  if ((rc = check_strides(v_stride, false, B, Hkv, Nkv)) != FA_OK) return rc;
+  if ((rc = check_strides(o_stride, true, B, Hq, Nq)) != FA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_LAYOUT;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_LAYOUT;
+  if (!extent_ok(B, Hq, Nq, D, q_stride) || !extent_ok(B, Hkv, Nkv, D, k_stride) ||
+      !extent_ok(B, Hkv, Nkv, D, v_stride) || !extent_ok(B, Hq, Nq, D, o_stride))
+    return FA_ERR_SHAPE;
+  p->q = q;
+  p->k = k;
+  p->v = v;
+  p->o = o;
+  p->lse = lse;
+  p->q_sb = q_stride[0]; p->q_sh = q_stride[1]; p->q_sn = q_stride[2];
+  p->k_sb = k_stride[0]; p->k_sh = k_stride[1]; p->k_sn = k_stride[2];
+  p->v_sb = v_stride[0]; p->v_sh = v_stride[1]; p->v_sn = v_stride[2];
+  p->o_sb = o_stride[0]; p->o_sh = o_stride[1]; p->o_sn = o_stride[2];
+  p->B = (int32_t)B;
+  p->Hq = (int32_t)Hq;
+  p->Hkv = (int32_t)Hkv;
+  p->Nq = (int32_t)Nq;
+  p->Nkv = (int32_t)Nkv;
+  p->group = (int32_t)(Hq / Hkv);
+  p->n_qtiles = (int32_t)n_qt;
+  // scores enter the base-2 softmax as s * scale * log2(e), one fp32 FMA per score
+  p->c = (float)((double)scale * 1.4426950408889634074);
+  p->win_left = (int32_t)Nq;
+  p->win_right = (int32_t)Nkv;
+  return FA_OK;
 }
 
 // ---- backward: per head dim, the dK/dV kernel (32 keys per wave, 64-row query tiles) and the
@@ -233,47 +280,35 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            int64_t Nq, int64_t Nkv, int64_t D, const int64_t q_stride[4], const int64_t k_stride[4],
            const int64_t v_stride[4], const int64_t o_stride[4], float scale, int causal, int dtype,
            void* stream) {
-  if (!q || !k || !v || !o || !lse || !q_stride || !k_stride || !v_stride || !o_stride) return FA_ERR_NULL;
-  PlanInfo pi;
-  int64_t n_qt = 0, grid = 0;
-  int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, causal != 0, &pi, &n_qt, &grid);
-  if (rc != FA_OK) return rc;
-  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_SCALE;
-  if ((rc = check_strides(q_stride, false, B, Hq, Nq)) != FA_OK) return rc;
-  if ((rc = check_strides(k_stride, false, B, Hkv, Nkv)) != FA_OK) return rc;
-  if ((rc = check_strides(v_stride, false, B, Hkv, Nkv)) != FA_OK) return rc;
-  if ((rc = check_strides(o_stride, true, B, Hq, Nq)) != FA_OK) return rc;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_LAYOUT;
-  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_LAYOUT;
-  if (!extent_ok(B, Hq, Nq, D, q_stride) || !extent_ok(B, Hkv, Nkv, D, k_stride) ||
-      !extent_ok(B, Hkv, Nkv, D, v_stride) || !extent_ok(B, Hq, Nq, D, o_stride))
-    return FA_ERR_SHAPE;
-
   FwdParams p;
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  p.lse = lse;
-  p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
-  p.k_sb = k_stride[0]; p.k_sh = k_stride[1]; p.k_sn = k_stride[2];
-  p.v_sb = v_stride[0]; p.v_sh = v_stride[1]; p.v_sn = v_stride[2];
-  p.o_sb = o_stride[0]; p.o_sh = o_stride[1]; p.o_sn = o_stride[2];
-  p.B = (int32_t)B;
-  p.Hq = (int32_t)Hq;
-  p.Hkv = (int32_t)Hkv;
-  p.Nq = (int32_t)Nq;
-  p.Nkv = (int32_t)Nkv;
-  p.group = (int32_t)(Hq / Hkv);
-  p.n_qtiles = (int32_t)n_qt;
-  // scores enter the base-2 softmax as s * scale * log2(e), one fp32 FMA per score
-  p.c = (float)((double)scale * 1.4426950408889634074);
-
+  int64_t grid = 0;
+  const int rc = prepare_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride, scale,
+                             causal != 0, dtype, &p, &grid);
+  if (rc != FA_OK) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool cz = causal != 0;
   if (dtype == FA_DTYPE_BF16)
     return cz ? launch_d<__bf16, true>(D, p, grid, s) : launch_d<__bf16, false>(D, p, grid, s);
   return cz ? launch_d<_Float16, true>(D, p, grid, s) : launch_d<_Float16, false>(D, p, grid, s);
+}
+
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                  int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, const int64_t q_stride[4],
+                  const int64_t k_stride[4], const int64_t v_stride[4], const int64_t o_stride[4], float scale,
+                  int64_t window_left, int64_t window_right, int dtype, void* stream) {
+  FwdParams p;
+  int64_t grid = 0;
+  const int rc = prepare_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride, scale,
+                             false, dtype, &p, &grid);
+  if (rc != FA_OK) return rc;
+  if (window_left < -1 || window_right < -1) return FA_ERR_SHAPE;
+  if (Nq > kMaxWindowSeq || Nkv > kMaxWindowSeq) return FA_ERR_SHAPE;
+  // a side wider than the sequences reaches every key, the same as an unbounded side
+  p.win_left = (int32_t)(window_left < 0 || window_left > Nq ? Nq : window_left);
+  p.win_right = (int32_t)(window_right < 0 || window_right > Nkv ? Nkv : window_right);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == FA_DTYPE_BF16) return launch_d<__bf16, false, true>(D, p, grid, s);
+  return launch_d<_Float16, false, true>(D, p, grid, s);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

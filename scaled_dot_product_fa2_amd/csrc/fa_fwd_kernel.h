@@ -88,6 +88,9 @@ struct FwdParams {
   int32_t group;     // Hq / Hkv
   int32_t n_qtiles;  // ceil(Nq / BQ)
   float c;           // scale * log2(e)
+  // sliding window (the WINDOW instances only): row i sees keys i - win_left .. i + win_right; an
+  // unbounded side is passed as Nq (left) or Nkv (right), which no row can reach past
+  int32_t win_left, win_right;
 };
 
 // Tile configuration: NW waves per workgroup, QB 32-row query blocks per wave,
@@ -169,7 +172,7 @@ constexpr int kPvLeadD256 = 3;  // one fragment less at D = 256, which is at the
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-template <typename T, bool CAUSAL, class Cfg>
+template <typename T, bool CAUSAL, class Cfg, bool WINDOW = false>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
     fa_fwd_kernel(const FwdParams p) {
@@ -228,6 +231,17 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     constexpr int Q_PARTS = BQ / BKV;
     static_assert(Q_PARTS >= 1 && Q_PARTS <= 4 && Q_PARTS * BKV == BQ, "Q tile must fit the four K/V buffers");
     constexpr bool KV0_WITH_Q = Q_PARTS <= 2;
+    // key tiles this item visits: [t0, t0 + n_tiles)
+    int t0 = 0, n_tiles;
+    if (WINDOW) {
+      const int q_last = min(q0 + BQ, p.Nq) - 1;
+      const int first = max(0, q0 - p.win_left);
+      const int last = min(p.Nkv - 1, q_last + p.win_right);
+      t0 = first / BKV;
+      n_tiles = first > last ? 0 : last / BKV + 1 - t0;
+    } else {
+      n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
+    }
     auto qpart = [&](int part) {
       if (KV0_WITH_Q) return part == 0 ? k_st1 : v_st1;
       return part == 0 ? k_st0 : part == 1 ? k_st1 : part == 2 ? v_st0 : v_st1;
@@ -238,9 +252,9 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       for (int part = 0; part < Q_PARTS; ++part)
         if (q0 + part * BKV < p.Nq)
           dma_tile<D, BKV, NW>(qpart(part), qbase, q_stride, q0 + part * BKV, p.Nq, wave_u, q_dma_off);
-      if (KV0_WITH_Q) {
-        dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, 0, p.Nkv, wave_u, k_dma_off);
-        dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, 0, p.Nkv, wave_u, v_dma_off);
+      if (KV0_WITH_Q && n_tiles > 0) {
+        dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, t0 * BKV, p.Nkv, wave_u, k_dma_off);
+        dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, t0 * BKV, p.Nkv, wave_u, v_dma_off);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -257,7 +271,6 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     }
     __syncthreads();  // the Q staging area takes K/V tiles below
 
-    const int n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
     // leading tiles in which every (row, key) pair of the workgroup is visible and in range
     int n_full = p.Nkv / BKV;
     if (CAUSAL && (q0 + 1) / BKV < n_full) n_full = (q0 + 1) / BKV;
@@ -277,9 +290,9 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     const int wq_last = wq_first + QB * 32 - 1;
     const float c = p.c;
 
-    if (!KV0_WITH_Q) {
-      dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, 0, p.Nkv, wave_u, k_dma_off);
-      dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, 0, p.Nkv, wave_u, v_dma_off);
+    if (!KV0_WITH_Q && n_tiles > 0) {
+      dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, t0 * BKV, p.Nkv, wave_u, k_dma_off);
+      dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, t0 * BKV, p.Nkv, wave_u, v_dma_off);
     }
     // per-lane parts of the fragment read offsets
     constexpr int KP = kfrag_parities<D>();
@@ -292,20 +305,25 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     // S^T = K Q^T, online softmax, O^T += V^T P^T.
     auto step = [&](auto stage_c, int j) {
       constexpr int S = decltype(stage_c)::value;
-      const bool mask = j >= n_full;  // wave-uniform
       lds_char_t* const kcur = S == 0 ? k_st0 : k_st1;
       lds_char_t* const vcur = S == 0 ? v_st0 : v_st1;
       lds_char_t* const knext = S == 0 ? k_st1 : k_st0;
       lds_char_t* const vnext = S == 0 ? v_st1 : v_st0;
-      const int kpos = j * BKV;
+      const int kpos = (t0 + j) * BKV;
+      // wave-uniform: does any (row, key) pair of this wave and tile fall outside the visible set?
+      const bool mask = WINDOW ? !(kpos >= wq_last - p.win_left && kpos + BKV - 1 <= wq_first + p.win_right &&
+                                   kpos + BKV <= p.Nkv)
+                               : j >= n_full;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (j + 1 < n_tiles) {
         dma_tile<D, BKV, NW>(knext, kbase, k_stride, kpos + BKV, p.Nkv, wave_u, k_dma_off);
         dma_tile<D, BKV, NW>(vnext, vbase, v_stride, kpos + BKV, p.Nkv, wave_u, v_dma_off);
       }
-      // a causal tile wholly to the right of this wave's last row contributes nothing
+      // a causal tile wholly to the right of this wave's last row contributes nothing; with a
+      // window, neither does a tile wholly outside every row's band
       if (CAUSAL && kpos > wq_last) return;
+      if (WINDOW && (kpos > wq_last + p.win_right || kpos + BKV - 1 < wq_first - p.win_left)) return;
 
       // ---- S^T = K Q^T
       f32x16 sc[QB][NKB];
@@ -349,12 +367,16 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           const int base = kpos + 4 * half;
           int limit = p.Nkv - 1 - base;
           if (CAUSAL) limit = min(limit, qrow - base);
+          if (WINDOW) limit = min(limit, qrow + p.win_right - base);
+          // with a window, keys below the band are hidden too: koff < lower
+          const int lower = WINDOW ? qrow - p.win_left - base : -1;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int koff = 32 * kb + 8 * (r >> 2) + (r & 3);
-              sc[qb][kb][r] = koff > limit ? -INFINITY : sc[qb][kb][r];
+              const bool hidden = WINDOW ? (koff > limit || koff < lower) : koff > limit;
+              sc[qb][kb][r] = hidden ? -INFINITY : sc[qb][kb][r];
             }
         }
         float mx = -INFINITY;
@@ -447,7 +469,9 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     for (int qb = 0; qb < QB; ++qb) {
       const int qrow = wq_first + qfrag_row(qb, lane);
       const float l_tot = wave_half_sum(l_run[qb]);
-      const float inv = 1.f / l_tot;
+      // a window can leave a row without visible keys: O = 0 and LSE = -inf there
+      const bool empty = WINDOW && !(l_tot > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_tot;
       if (qrow < p.Nq) {
         char* orow = (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn) * 2;
 #pragma unroll
@@ -460,7 +484,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
             const int col = 32 * db + acc_row(4 * g4, lane);
             *(i32x2*)(orow + col * 2) = __builtin_bit_cast(i32x2, ov);
           }
-        if (half == 0) p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] = (m_run[qb] + __log2f(l_tot)) * LN2;
+        if (half == 0)
+          p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] = empty ? -INFINITY : (m_run[qb] + __log2f(l_tot)) * LN2;
       }
     }
   }  // item loop

@@ -181,3 +181,22 @@ BWD_BAD = [
 @pytest.mark.parametrize("name,over,code", BWD_BAD, ids=[b[0] for b in BWD_BAD])
 def test_bwd_validation_rejects(name, over, code):
     assert _bwd_call(**over) == D_[code]
+
+
+def _win_call(left, right, **over):
+    a = dict(VALID)
+    a.update(over)
+    lib = _lib()
+    return lib.fa_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"],
+                             a["D"], _st(*a["qs"]), _st(*a["ks"]), _st(*a["vs"]), _st(*a["os"]), a["scale"], left, right,
+                             a["dtype"], None)
+
+
+@pytest.mark.parametrize("left,right,over,code", [
+    (-2, 0, {}, "FA_ERR_SHAPE"), (0, -5, {}, "FA_ERR_SHAPE"),
+    (4, 4, dict(Nq=(1 << 30) + 1, qs=(0, 64 * ((1 << 30) + 1), 64, 1), os=(0, 64 * ((1 << 30) + 1), 64, 1)),
+     "FA_ERR_SHAPE"),
+    (4, 4, dict(D=48), "FA_ERR_HEAD_DIM"), (4, 4, dict(q=0), "FA_ERR_NULL"), (4, 4, dict(scale=0.0), "FA_ERR_SCALE"),
+], ids=["left_below_minus1", "right_below_minus1", "nq_over_2p30", "head_dim", "null_q", "scale"])
+def test_window_validation_rejects(left, right, over, code):
+    assert _win_call(left, right, **over) == D_[code]
