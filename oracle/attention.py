@@ -48,7 +48,7 @@ from typing import Iterable, Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["attention_ref", "attention_rows", "attention_ref_pool", "head_ref"]
+__all__ = ["attention_ref", "attention_rows", "attention_ref_pool", "head_ref", "attention_varlen_ref"]
 
 
 def _f64(x) -> np.ndarray:
@@ -207,3 +207,36 @@ def attention_ref_pool(q, k, v, *, causal: bool, scale: Optional[float] = None,
         for unit, res in ex.map(_pool_unit, units):
             out[unit] = res
     return out, workers
+
+
+def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool,
+                         scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention over packed variable-length sequences, in float64.
+
+    The CSR layout named in "Write Triton Attention Kernel" (Inputs, item 6; Correctness
+    requirements: the key loop of a batch element ends at that element's own length):
+    q: (total_q, Hq, D), k: (total_k, Hkv, D), v: (total_k, Hkv, Dv); sequence b owns query tokens
+    cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 and key tokens cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1,
+    positions counted from the start of its own sequence (so the causal mask is top-left per
+    sequence). Returns o (total_q, Hq, Dv) and lse (Hq, total_q). A sequence with no keys gives its
+    rows o = 0 and lse = -inf.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    if len(cq) != len(ck) or cq[0] != 0 or ck[0] != 0 or cq[-1] != q.shape[0] or ck[-1] != k.shape[0]:
+        raise ValueError("cu_seqlens must start at 0 and end at the token counts, one entry per sequence + 1")
+    Hq, Dv = q.shape[1], v.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[2])
+    o = np.zeros((q.shape[0], Hq, Dv), dtype=np.float64)
+    lse = np.full((Hq, q.shape[0]), -np.inf, dtype=np.float64)
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 <= q0 or k1 <= k0:
+            continue                      # no rows, or rows without keys (o = 0, lse = -inf)
+        ob, lb = attention_ref(q[q0:q1].transpose(1, 0, 2)[None], k[k0:k1].transpose(1, 0, 2)[None],
+                               v[k0:k1].transpose(1, 0, 2)[None], causal=causal, scale=scale)
+        o[q0:q1] = ob[0].transpose(1, 0, 2)
+        lse[:, q0:q1] = lb[0]
+    return o, lse

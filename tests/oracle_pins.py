@@ -460,10 +460,62 @@ def pin_window_special_cases(mod):
     _close(l_r, l_a[0, 1, rows], what="window rows lse")
 
 
+# ---------------------------------------------------------------------------------------------
+# Packed variable-length sequences (CSR offsets).
+
+def pin_varlen_against_masked_sdpa(mod):
+    """Packed sequences = one padded batch whose padding keys are masked out, computed by torch
+    float64 SDPA with a boolean mask (causal positions counted per sequence)."""
+    rng = _rng(41)
+    lens_q = [5, 1, 9, 0, 7]
+    lens_k = [5, 4, 12, 3, 7]
+    Hq, Hkv, D = 4, 2, 8
+    cq = np.concatenate([[0], np.cumsum(lens_q)])
+    ck = np.concatenate([[0], np.cumsum(lens_k)])
+    q = _rand(rng, int(cq[-1]), Hq, D)
+    k = _rand(rng, int(ck[-1]), Hkv, D)
+    v = _rand(rng, int(ck[-1]), Hkv, D)
+    for causal in (False, True):
+        o, lse = mod.attention_varlen_ref(q, k, v, cq, ck, causal=causal, scale=0.45)
+        for b in range(len(lens_q)):
+            nq, nk = lens_q[b], lens_k[b]
+            if nq == 0:
+                continue
+            qb = torch.from_numpy(q[cq[b]:cq[b + 1]].transpose(1, 0, 2).copy())[None]
+            kb = torch.from_numpy(k[ck[b]:ck[b + 1]].transpose(1, 0, 2).copy())[None]
+            vb = torch.from_numpy(v[ck[b]:ck[b + 1]].transpose(1, 0, 2).copy())[None]
+            mask = torch.ones(nq, nk, dtype=torch.bool)
+            if causal:
+                mask = torch.tril(mask)
+            ref = torch.nn.functional.scaled_dot_product_attention(qb, kb, vb, attn_mask=mask, scale=0.45,
+                                                                   enable_gqa=True)[0].numpy().transpose(1, 0, 2)
+            _close(o[cq[b]:cq[b + 1]], ref, tol=1e-10, what=f"varlen seq {b} causal={causal}")
+            s = 0.45 * np.einsum("ihd,jhd->hij", q[cq[b]:cq[b + 1]], np.repeat(k[ck[b]:ck[b + 1]], Hq // Hkv, axis=1))
+            if causal:
+                s = np.where(np.tril(np.ones((nq, nk), dtype=bool)), s, -np.inf)
+            _close(lse[:, cq[b]:cq[b + 1]], logsumexp(s, axis=-1), what=f"varlen lse seq {b}")
+
+
+def pin_varlen_single_and_empty(mod):
+    """One sequence is the dense computation; a sequence without keys gives o = 0, lse = -inf."""
+    rng = _rng(42)
+    q = _rand(rng, 11, 2, 4)
+    k = _rand(rng, 13, 2, 4)
+    v = _rand(rng, 13, 2, 4)
+    o, lse = mod.attention_varlen_ref(q, k, v, [0, 11], [0, 13], causal=True, scale=0.7)
+    od, ld = mod.attention_ref(q.transpose(1, 0, 2)[None], k.transpose(1, 0, 2)[None], v.transpose(1, 0, 2)[None],
+                               causal=True, scale=0.7)
+    _close(o, od[0].transpose(1, 0, 2), what="varlen single o")
+    _close(lse, ld[0], what="varlen single lse")
+    o2, l2 = mod.attention_varlen_ref(q, k, v, [0, 4, 11], [0, 13, 13], causal=False, scale=0.7)
+    assert np.all(o2[4:] == 0.0) and np.all(np.isneginf(l2[:, 4:])), "rows of a key-less sequence"
+
+
 ALL_PINS = [
     pin_brute_force, pin_sdpa_float64, pin_lse_scipy, pin_single_key, pin_zero_query,
     pin_first_causal_row, pin_default_scale, pin_scale_moves_to_q, pin_convex_rows, pin_affine_v,
     pin_key_shift, pin_gqa_is_repeated_mha, pin_causal_prefix, pin_key_permutation,
     pin_two_block_merge, pin_strided_views, pin_rows_agree, pin_large_scores,
     pin_window_brute_force, pin_window_sdpa_bool_mask, pin_window_special_cases,
+    pin_varlen_against_masked_sdpa, pin_varlen_single_and_empty,
 ]

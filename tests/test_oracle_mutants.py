@@ -36,6 +36,8 @@ MUTANTS = [
     ("window_right_ignored", "if right is not None:\n                s", "if False:\n                s"),
     ("window_right_as_left", "r[:, None] + right, s", "r[:, None] + left, s"),
     ("empty_row_lse_zero", "np.where(empty, -np.inf,", "np.where(empty, 0.0,"),
+    ("varlen_keys_shifted", "k[k0:k1].transpose(1, 0, 2)[None],", "k[k0 + 1:k1 + 1].transpose(1, 0, 2)[None],"),
+    ("varlen_q_offsets_for_keys", "v[k0:k1].transpose(1, 0, 2)[None]", "v[q0:q0 + k1 - k0].transpose(1, 0, 2)[None]"),
 ]
 
 
