@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 /* Element types of Q, K, V and O (all four share one type). */
 #define FA_DTYPE_F16 0
@@ -101,6 +101,34 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
                   const int64_t q_stride[4], const int64_t k_stride[4],
                   const int64_t v_stride[4], const int64_t o_stride[4],
                   float scale, int64_t window_left, int64_t window_right, int dtype, void* stream);
+
+/*
+ * fa_fwd_varlen - the forward over packed variable-length sequences (the CSR layout "Write
+ * Triton Attention Kernel" lists among its inputs, item 6; per its correctness requirements each
+ * sequence's key loop ends at that sequence's own length and padding never contributes).
+ *
+ * q   : (total_q, Hq, D) token-major, strides q_stride = {token, head, dim} in elements
+ * k, v: (total_k, Hkv, D), strides k_stride / v_stride likewise
+ * o   : (total_q, Hq, D), strides o_stride
+ * lse : fp32, contiguous (Hq, total_q): lse[h * total_q + token]
+ * cu_seqlens_q, cu_seqlens_k : device int32 arrays of B + 1 offsets; sequence b owns query tokens
+ *       [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key/value tokens [cu_seqlens_k[b], cu_seqlens_k[b+1]).
+ *       The caller guarantees 0 = cu[0] <= cu[1] <= ... <= cu[B] = total and every length <= the
+ *       matching max_seqlen; the kernel clamps offsets to [0, total] and lengths to max_seqlen, so
+ *       arrays breaking this give unspecified values but never an access outside the tensors.
+ * max_seqlen_q, max_seqlen_k : the longest sequence lengths (>= 1, <= the totals); they size the grid.
+ * causal: top-left causal mask per sequence (positions counted from each sequence's start).
+ * A sequence with queries but no keys gets O = 0 and LSE = -inf on its rows. Other rules
+ * (dtype, head dims, GQA, 16-byte strides and pointers, scale, stream, ownership, errors) as in
+ * fa_fwd; 1 <= total_q, total_k < 2^31.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t total_q, int64_t total_k,
+                  int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D,
+                  const int64_t q_stride[3], const int64_t k_stride[3],
+                  const int64_t v_stride[3], const int64_t o_stride[3],
+                  float scale, int causal, int dtype, void* stream);
 
 /*
  * fa_bwd - enqueue the attention backward on `stream` and return: given the

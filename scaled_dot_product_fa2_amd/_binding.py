@@ -48,6 +48,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p, f32,
                                   i64, i64, i32, vp]
     lib.fa_fwd_window.restype = i32
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64p, i64p,
+                                  i64p, i64p, f32, i32, i32, vp]
+    lib.fa_fwd_varlen.restype = i32
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                            i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f32, i32, i32, vp]
     lib.fa_bwd.restype = i32
@@ -246,5 +249,53 @@ def fa_fwd_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, window_l
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
         B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(out),
         float(scale), int(window_left), int(window_right), _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return out, lse
+
+
+def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                  cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, *, causal: bool = False,
+                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward over packed variable-length sequences.
+
+    q: (total_q, Hq, D), k, v: (total_k, Hkv, D) token-major GPU tensors; cu_seqlens_q/k: int32 GPU
+    tensors of B + 1 offsets. Returns o (total_q, Hq, D) and lse (Hq, total_q) float32.
+    """
+    if not all(t.is_cuda for t in (q, k, v, cu_seqlens_q, cu_seqlens_k)):
+        raise ValueError("all tensors must be on the GPU")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if not (cu_seqlens_q.is_contiguous() and cu_seqlens_k.is_contiguous()) or cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be contiguous with B + 1 entries each")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, _ = k.shape
+    if k.shape != (total_k, Hkv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be (total_k, Hkv, D) with q's head dim")
+    B = cu_seqlens_q.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must match q in shape, dtype and device")
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    elif lse.shape != (Hq, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (Hq, total_q) tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+
+    def st3(t):
+        return (ctypes.c_int64 * 3)(*t.stride())
+
+    code = load_library().fa_fwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
+        cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D,
+        st3(q), st3(k), st3(v), st3(out), float(scale), int(bool(causal)), _DTYPES[q.dtype],
+        ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return out, lse

@@ -106,22 +106,22 @@ int check_strides(const int64_t* st, bool is_output, int64_t B, int64_t H, int64
   return FA_OK;
 }
 
-template <typename T, bool CAUSAL, int D, bool WINDOW = false>
+template <typename T, bool CAUSAL, int D, bool WINDOW = false, bool VARLEN = false>
 int launch(const FwdParams& p, int64_t grid, hipStream_t stream) {
   typedef typename CfgFor<D>::type C;
-  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, CAUSAL, C, WINDOW>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
-                     p);
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, CAUSAL, C, WINDOW, VARLEN>), dim3((unsigned)grid), dim3(C::THREADS), 0,
+                     stream, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-template <typename T, bool CAUSAL, bool WINDOW = false>
+template <typename T, bool CAUSAL, bool WINDOW = false, bool VARLEN = false>
 int launch_d(int64_t D, const FwdParams& p, int64_t grid, hipStream_t stream) {
   switch (D) {
-    case 16: return launch<T, CAUSAL, 16, WINDOW>(p, grid, stream);
-    case 32: return launch<T, CAUSAL, 32, WINDOW>(p, grid, stream);
-    case 64: return launch<T, CAUSAL, 64, WINDOW>(p, grid, stream);
-    case 128: return launch<T, CAUSAL, 128, WINDOW>(p, grid, stream);
-    case 256: return launch<T, CAUSAL, 256, WINDOW>(p, grid, stream);
+    case 16: return launch<T, CAUSAL, 16, WINDOW, VARLEN>(p, grid, stream);
+    case 32: return launch<T, CAUSAL, 32, WINDOW, VARLEN>(p, grid, stream);
+    case 64: return launch<T, CAUSAL, 64, WINDOW, VARLEN>(p, grid, stream);
+    case 128: return launch<T, CAUSAL, 128, WINDOW, VARLEN>(p, grid, stream);
+    case 256: return launch<T, CAUSAL, 256, WINDOW, VARLEN>(p, grid, stream);
     default: return FA_ERR_HEAD_DIM;
   }
 }
@@ -166,6 +166,12 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   p->c = (float)((double)scale * 1.4426950408889634074);
   p->win_left = (int32_t)Nq;
   p->win_right = (int32_t)Nkv;
+  p->cu_q = nullptr;
+  p->cu_k = nullptr;
+  p->total_q = 0;
+  p->total_k = 0;
+  p->lse_sb = Hq * Nq;
+  p->lse_sh = Nq;
   return FA_OK;
 }
 
@@ -309,6 +315,53 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == FA_DTYPE_BF16) return launch_d<__bf16, false, true>(D, p, grid, s);
   return launch_d<_Float16, false, true>(D, p, grid, s);
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, int64_t B, int64_t Hq, int64_t Hkv, int64_t total_q,
+                  int64_t total_k, int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D,
+                  const int64_t q_stride[3], const int64_t k_stride[3], const int64_t v_stride[3],
+                  const int64_t o_stride[3], float scale, int causal, int dtype, void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k || !q_stride || !k_stride || !v_stride || !o_stride) return FA_ERR_NULL;
+  if (total_q < 1 || total_k < 1 || total_q > kMaxDim || total_k > kMaxDim) return FA_ERR_SHAPE;
+  if (max_seqlen_q < 1 || max_seqlen_k < 1 || max_seqlen_q > total_q || max_seqlen_k > total_k) return FA_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) != 0 || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u) != 0)
+    return FA_ERR_LAYOUT;
+  // token-major tensors: strides (token, head, dim), viewed as one batch of total tokens for the
+  // layout and extent checks, and as B sequences with batch stride 0 by the kernel
+  const int64_t qs[4] = {0, q_stride[1], q_stride[0], q_stride[2]};
+  const int64_t ks[4] = {0, k_stride[1], k_stride[0], k_stride[2]};
+  const int64_t vs[4] = {0, v_stride[1], v_stride[0], v_stride[2]};
+  const int64_t os[4] = {0, o_stride[1], o_stride[0], o_stride[2]};
+  if (!extent_ok(1, Hq, total_q, D, qs) || !extent_ok(1, Hkv, total_k, D, ks) || !extent_ok(1, Hkv, total_k, D, vs) ||
+      !extent_ok(1, Hq, total_q, D, os))
+    return FA_ERR_SHAPE;
+  int64_t lse_n;
+  if (!mul_ok(Hq, total_q, &lse_n) || lse_n > ((int64_t)1 << 62)) return FA_ERR_SHAPE;
+  // strides, alignment and scale as one sequence of the longest lengths, then the grid for B sequences
+  FwdParams p;
+  int64_t grid = 0;
+  int rc = prepare_fwd(q, k, v, o, lse, 1, Hq, Hkv, max_seqlen_q, max_seqlen_k, D, qs, ks, vs, os, scale, causal != 0,
+                       dtype, &p, &grid);
+  if (rc != FA_OK) return rc;
+  PlanInfo pi;
+  int64_t n_qt = 0;
+  if ((rc = check_shape(B, Hq, Hkv, max_seqlen_q, max_seqlen_k, D, dtype, causal != 0, &pi, &n_qt, &grid)) != FA_OK)
+    return rc;
+  p.B = (int32_t)B;
+  p.n_qtiles = (int32_t)n_qt;
+  if (B + 1 > kMaxDim) return FA_ERR_SHAPE;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = (int32_t)total_q;
+  p.total_k = (int32_t)total_k;
+  p.lse_sb = 0;
+  p.lse_sh = total_q;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool cz = causal != 0;
+  if (dtype == FA_DTYPE_BF16)
+    return cz ? launch_d<__bf16, true, false, true>(D, p, grid, s) : launch_d<__bf16, false, false, true>(D, p, grid, s);
+  return cz ? launch_d<_Float16, true, false, true>(D, p, grid, s) : launch_d<_Float16, false, false, true>(D, p, grid, s);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

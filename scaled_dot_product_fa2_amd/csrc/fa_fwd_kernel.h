@@ -91,6 +91,13 @@ struct FwdParams {
   // sliding window (the WINDOW instances only): row i sees keys i - win_left .. i + win_right; an
   // unbounded side is passed as Nq (left) or Nkv (right), which no row can reach past
   int32_t win_left, win_right;
+  // packed variable-length sequences (the VARLEN instances only): sequence b owns tokens
+  // cu_q[b] .. cu_q[b+1]-1 of Q/O and cu_k[b] .. cu_k[b+1]-1 of K/V; Nq and Nkv hold the longest
+  // lengths, the batch strides are 0
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t total_q, total_k;
+  int64_t lse_sb, lse_sh;  // LSE element offset of (b, h); the row index is added to it
 };
 
 // Tile configuration: NW waves per workgroup, QB 32-row query blocks per wave,
@@ -172,7 +179,7 @@ constexpr int kPvLeadD256 = 3;  // one fragment less at D = 256, which is at the
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-template <typename T, bool CAUSAL, class Cfg, bool WINDOW = false>
+template <typename T, bool CAUSAL, class Cfg, bool WINDOW = false, bool VARLEN = false>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
     fa_fwd_kernel(const FwdParams p) {
@@ -212,11 +219,26 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     const int b = item.b, h = item.h, qt = item.qt;
     const int kvh = h / p.group;
     const int q0 = qt * BQ;
+    // the item's sequence lengths and first tokens; packed sequences read them from the offsets,
+    // clamped to the token counts so that no offset array can send a copy out of bounds
+    int nq = p.Nq, nkv = p.Nkv, q_tok0 = 0, k_tok0 = 0;
+    if (VARLEN) {
+      const int cq0 = min(max(p.cu_q[b], 0), p.total_q), cq1 = min(max(p.cu_q[b + 1], cq0), p.total_q);
+      const int ck0 = min(max(p.cu_k[b], 0), p.total_k), ck1 = min(max(p.cu_k[b + 1], ck0), p.total_k);
+      q_tok0 = cq0;
+      k_tok0 = ck0;
+      nq = min(cq1 - cq0, p.Nq);
+      nkv = min(ck1 - ck0, p.Nkv);
+      if (q0 >= nq) continue;  // a query tile past this sequence's end
+    }
     __syncthreads();  // every wave is done with the previous item's LDS tiles
 
-    const char* qbase = (const char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
-    const char* kbase = (const char*)p.k + ((int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh) * 2;
-    const char* vbase = (const char*)p.v + ((int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh) * 2;
+    const char* qbase =
+        (const char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)q_tok0 * p.q_sn) * 2;
+    const char* kbase =
+        (const char*)p.k + ((int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + (int64_t)k_tok0 * p.k_sn) * 2;
+    const char* vbase =
+        (const char*)p.v + ((int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + (int64_t)k_tok0 * p.v_sn) * 2;
 
     // Row strides in bytes (validated on the host to keep every tile offset in 31 bits).
     const int q_stride = (int)(p.q_sn * 2), k_stride = (int)(p.k_sn * 2), v_stride = (int)(p.v_sn * 2);
@@ -234,13 +256,13 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     // key tiles this item visits: [t0, t0 + n_tiles)
     int t0 = 0, n_tiles;
     if (WINDOW) {
-      const int q_last = min(q0 + BQ, p.Nq) - 1;
+      const int q_last = min(q0 + BQ, nq) - 1;
       const int first = max(0, q0 - p.win_left);
-      const int last = min(p.Nkv - 1, q_last + p.win_right);
+      const int last = min(nkv - 1, q_last + p.win_right);
       t0 = first / BKV;
       n_tiles = first > last ? 0 : last / BKV + 1 - t0;
     } else {
-      n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
+      n_tiles = (int)kv_tiles_for_qtile(q0, BQ, nkv, BKV, CAUSAL);
     }
     auto qpart = [&](int part) {
       if (KV0_WITH_Q) return part == 0 ? k_st1 : v_st1;
@@ -250,11 +272,11 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       const int q_dma_off = (int)dma_lane_offset<D, false>(lane, q_stride);
 #pragma unroll
       for (int part = 0; part < Q_PARTS; ++part)
-        if (q0 + part * BKV < p.Nq)
-          dma_tile<D, BKV, NW>(qpart(part), qbase, q_stride, q0 + part * BKV, p.Nq, wave_u, q_dma_off);
+        if (q0 + part * BKV < nq)
+          dma_tile<D, BKV, NW>(qpart(part), qbase, q_stride, q0 + part * BKV, nq, wave_u, q_dma_off);
       if (KV0_WITH_Q && n_tiles > 0) {
-        dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, t0 * BKV, p.Nkv, wave_u, k_dma_off);
-        dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, t0 * BKV, p.Nkv, wave_u, v_dma_off);
+        dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, t0 * BKV, nkv, wave_u, k_dma_off);
+        dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, t0 * BKV, nkv, wave_u, v_dma_off);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -272,7 +294,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     __syncthreads();  // the Q staging area takes K/V tiles below
 
     // leading tiles in which every (row, key) pair of the workgroup is visible and in range
-    int n_full = p.Nkv / BKV;
+    int n_full = nkv / BKV;
     if (CAUSAL && (q0 + 1) / BKV < n_full) n_full = (q0 + 1) / BKV;
     if (n_full > n_tiles) n_full = n_tiles;
 
@@ -291,8 +313,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     const float c = p.c;
 
     if (!KV0_WITH_Q && n_tiles > 0) {
-      dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, t0 * BKV, p.Nkv, wave_u, k_dma_off);
-      dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, t0 * BKV, p.Nkv, wave_u, v_dma_off);
+      dma_tile<D, BKV, NW>(k_st0, kbase, k_stride, t0 * BKV, nkv, wave_u, k_dma_off);
+      dma_tile<D, BKV, NW>(v_st0, vbase, v_stride, t0 * BKV, nkv, wave_u, v_dma_off);
     }
     // per-lane parts of the fragment read offsets
     constexpr int KP = kfrag_parities<D>();
@@ -312,13 +334,13 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       const int kpos = (t0 + j) * BKV;
       // wave-uniform: does any (row, key) pair of this wave and tile fall outside the visible set?
       const bool mask = WINDOW ? !(kpos >= wq_last - p.win_left && kpos + BKV - 1 <= wq_first + p.win_right &&
-                                   kpos + BKV <= p.Nkv)
+                                   kpos + BKV <= nkv)
                                : j >= n_full;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (j + 1 < n_tiles) {
-        dma_tile<D, BKV, NW>(knext, kbase, k_stride, kpos + BKV, p.Nkv, wave_u, k_dma_off);
-        dma_tile<D, BKV, NW>(vnext, vbase, v_stride, kpos + BKV, p.Nkv, wave_u, v_dma_off);
+        dma_tile<D, BKV, NW>(knext, kbase, k_stride, kpos + BKV, nkv, wave_u, k_dma_off);
+        dma_tile<D, BKV, NW>(vnext, vbase, v_stride, kpos + BKV, nkv, wave_u, v_dma_off);
       }
       // a causal tile wholly to the right of this wave's last row contributes nothing; with a
       // window, neither does a tile wholly outside every row's band
@@ -365,7 +387,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           // sequence end (key < Nkv) into one per-lane value.
           const int qrow = wq_first + qfrag_row(qb, lane);
           const int base = kpos + 4 * half;
-          int limit = p.Nkv - 1 - base;
+          int limit = nkv - 1 - base;
           if (CAUSAL) limit = min(limit, qrow - base);
           if (WINDOW) limit = min(limit, qrow + p.win_right - base);
           // with a window, keys below the band are hidden too: koff < lower
@@ -469,11 +491,13 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     for (int qb = 0; qb < QB; ++qb) {
       const int qrow = wq_first + qfrag_row(qb, lane);
       const float l_tot = wave_half_sum(l_run[qb]);
-      // a window can leave a row without visible keys: O = 0 and LSE = -inf there
-      const bool empty = WINDOW && !(l_tot > 0.f);
+      // a window, or a packed sequence without keys, can leave a row without visible keys:
+      // O = 0 and LSE = -inf there
+      const bool empty = (WINDOW || VARLEN) && !(l_tot > 0.f);
       const float inv = empty ? 0.f : 1.f / l_tot;
-      if (qrow < p.Nq) {
-        char* orow = (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn) * 2;
+      if (qrow < nq) {
+        char* orow =
+            (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)(q_tok0 + qrow) * p.o_sn) * 2;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -485,7 +509,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
             *(i32x2*)(orow + col * 2) = __builtin_bit_cast(i32x2, ov);
           }
         if (half == 0)
-          p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] = empty ? -INFINITY : (m_run[qb] + __log2f(l_tot)) * LN2;
+          p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + q_tok0 + qrow] =
+              empty ? -INFINITY : (m_run[qb] + __log2f(l_tot)) * LN2;
       }
     }
   }  // item loop

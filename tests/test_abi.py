@@ -200,3 +200,32 @@ def _win_call(left, right, **over):
 ], ids=["left_below_minus1", "right_below_minus1", "nq_over_2p30", "head_dim", "null_q", "scale"])
 def test_window_validation_rejects(left, right, over, code):
     assert _win_call(left, right, **over) == D_[code]
+
+
+VL = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=0x50000, cq=0x60000, ck=0x61000, B=3, Hq=4, Hkv=2,
+          tq=300, tk=400, mq=150, mk=200, D=64, qs=(256, 64, 1), ks=(128, 64, 1), vs=(128, 64, 1), os=(256, 64, 1),
+          scale=0.125, causal=1, dtype=0)
+
+
+def _vl_call(**over):
+    a = dict(VL)
+    a.update(over)
+    st3 = lambda s: (ctypes.c_int64 * 3)(*s) if s else None
+    return _lib().fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["B"], a["Hq"], a["Hkv"],
+                                a["tq"], a["tk"], a["mq"], a["mk"], a["D"], st3(a["qs"]), st3(a["ks"]), st3(a["vs"]),
+                                st3(a["os"]), a["scale"], a["causal"], a["dtype"], None)
+
+
+VL_BAD = [
+    ("null_cu", dict(cq=0), "FA_ERR_NULL"), ("null_stride", dict(ks=None), "FA_ERR_NULL"),
+    ("zero_total", dict(tq=0), "FA_ERR_SHAPE"), ("max_over_total", dict(mk=401), "FA_ERR_SHAPE"),
+    ("zero_max", dict(mq=0), "FA_ERR_SHAPE"), ("misaligned_cu", dict(ck=0x61002), "FA_ERR_LAYOUT"),
+    ("head_dim", dict(D=40), "FA_ERR_HEAD_DIM"), ("gqa", dict(Hq=3), "FA_ERR_GQA"),
+    ("dim_stride", dict(qs=(256, 64, 2)), "FA_ERR_LAYOUT"), ("dtype", dict(dtype=9), "FA_ERR_DTYPE"),
+    ("extent_overflow", dict(qs=(1 << 55, 64, 1)), "FA_ERR_SHAPE"),
+]
+
+
+@pytest.mark.parametrize("name,over,code", VL_BAD, ids=[b[0] for b in VL_BAD])
+def test_varlen_validation_rejects(name, over, code):
+    assert _vl_call(**over) == D_[code]
