@@ -154,7 +154,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * scale, causal, dtype, stream, and the stride and alignment rules: as in fa_fwd,
  *              with o and dout read-only inputs and dq, dk, dv outputs (no zero strides).
  *
- * Sizes as in fa_fwd, and B, Hq <= 65535. Ownership: the caller owns every
+ * Sizes as in fa_fwd, and ceil(N/128) * heads * B < 2^31 for both sequences. Ownership: the caller owns every
  * buffer; outputs and the workspace must not overlap any input or each other.
  * The library allocates nothing and never synchronises. Three kernels are
  * enqueued in order (Delta, then dK/dV, then dQ). Validation errors return

@@ -194,18 +194,24 @@ struct BwdCfgFor {
   typedef fa::BwdCfg<D, 4, D >= 256 ? 32 : 64, W_Q> dq;
 };
 
-constexpr int64_t kMaxGridYZ = 65535;
 
 template <typename T, bool CAUSAL, int D>
-int launch_bwd(const fa::BwdParams& p, hipStream_t stream) {
+int launch_bwd(fa::BwdParams p, hipStream_t stream) {
   typedef typename BwdCfgFor<D>::dkdv CK;
   typedef typename BwdCfgFor<D>::dq CQ;
+  // row block slowest under the causal mask (longest first), and when a grid is at most about two
+  // rounds of resident workgroups (the blocks of a head then run together on one XCD and share its
+  // streamed tiles in L2); otherwise the blocks of a head are dispatched consecutively
+  const int64_t kv_wgs = (int64_t)((p.Nkv + CK::BW - 1) / CK::BW) * p.Hkv * p.B;
+  const int64_t q_wgs = (int64_t)((p.Nq + CQ::BW - 1) / CQ::BW) * p.Hq * p.B;
+  p.dkdv_block_slowest = CAUSAL || kv_wgs <= 2 * kNumCUs * (CK::WAVES_PER_SIMD * 4 / CK::NW);
+  p.dq_block_slowest = CAUSAL || q_wgs <= 2 * kNumCUs * (CQ::WAVES_PER_SIMD * 4 / CQ::NW);
   constexpr int RPB = 256 / (D / 8);
   const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
   hipLaunchKernelGGL((fa::fa_bwd_delta_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                      stream, p);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  const dim3 kv_grid((unsigned)((p.Nkv + CK::BW - 1) / CK::BW), (unsigned)p.Hkv, (unsigned)p.B);
+  const dim3 kv_grid((unsigned)((int64_t)((p.Nkv + CK::BW - 1) / CK::BW) * p.Hkv * p.B));
   if constexpr (BwdCfgFor<D>::SPLIT_KV) {
     hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyV>), kv_grid, dim3(CK::THREADS), 0,
                        stream, p);
@@ -218,7 +224,7 @@ int launch_bwd(const fa::BwdParams& p, hipStream_t stream) {
   }
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<T, CAUSAL, CQ>),
-                     dim3((unsigned)((p.Nq + CQ::BW - 1) / CQ::BW), (unsigned)p.Hq, (unsigned)p.B),
+                     dim3((unsigned)((int64_t)((p.Nq + CQ::BW - 1) / CQ::BW) * p.Hq * p.B)),
                      dim3(CQ::THREADS), 0, stream, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -377,7 +383,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   int64_t n_qt = 0, grid = 0;
   int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, causal != 0, &pi, &n_qt, &grid);
   if (rc != FA_OK) return rc;
-  if (B > kMaxGridYZ || Hq > kMaxGridYZ) return FA_ERR_SHAPE;
+  // the gradient kernels use 1-D grids of (row block, head, batch) workgroups
+  if (((Nkv + 127) / 128) * Hkv * B > kMaxDim || ((Nq + 127) / 128) * Hq * B > kMaxDim) return FA_ERR_SHAPE;
   if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_SCALE;
   if ((rc = check_strides(q_stride, false, B, Hq, Nq)) != FA_OK) return rc;
   if ((rc = check_strides(k_stride, false, B, Hkv, Nkv)) != FA_OK) return rc;

@@ -57,6 +57,9 @@ struct BwdParams {
   int32_t group;  // Hq / Hkv
   float c;        // scale * log2(e)
   float scale;
+  // order of the 1-D gradient grids: nonzero = row block slowest (longest first under the causal
+  // mask; L2 sharing between the blocks of a head when the grid is about one wave of workgroups)
+  int32_t dkdv_block_slowest, dq_block_slowest;
 };
 
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -115,7 +118,7 @@ struct BwdCfg {
 };
 
 // ------------------------------------------------------------------------------------------------
-// dK, dV. Grid: (ceil(Nkv / BW), Hkv, B). PART selects the outputs: kBwdBoth, or one of
+// dK, dV. Grid: ceil(Nkv / BW) * Hkv * B workgroups (1-D). PART selects the outputs: kBwdBoth, or one of
 // kBwdOnlyV / kBwdOnlyK (two launches, S recomputed in each, to fit wide heads in registers).
 constexpr int kBwdBoth = 0, kBwdOnlyV = 1, kBwdOnlyK = 2;
 
@@ -147,8 +150,23 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int b = blockIdx.z, kvh = blockIdx.y;
-  const int k0 = blockIdx.x * BK;
+  // 1-D grid over (key block, kv head, batch). Key block slowest: under the causal mask the early
+  // key blocks, which see the most query tiles, are dispatched first (longest first). Key block
+  // fastest: the key blocks of one head are dispatched together and share its Q/dO stream in cache.
+  const int64_t lin = blockIdx.x;
+  const int n_kb = (p.Nkv + BK - 1) / BK;
+  int kvh, b, k0;
+  if (p.dkdv_block_slowest) {
+    const int64_t per_kb = (int64_t)p.Hkv * p.B;
+    kvh = (int)(lin % p.Hkv);
+    b = (int)((lin % per_kb) / p.Hkv);
+    k0 = (int)(lin / per_kb) * BK;
+  } else {
+    const int64_t rest = lin / n_kb;
+    k0 = (int)(lin % n_kb) * BK;
+    kvh = (int)(rest % p.Hkv);
+    b = (int)(rest / p.Hkv);
+  }
   const int kw0 = k0 + 32 * wave;  // first key of this wave
   const int my_key = kw0 + (lane & 31);
 
@@ -354,7 +372,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
 }
 
 // ------------------------------------------------------------------------------------------------
-// dQ. Grid: (ceil(Nq / BW), Hq, B).
+// dQ. Grid: ceil(Nq / BW) * Hq * B workgroups (1-D).
 template <typename T, bool CAUSAL, class Cfg>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
@@ -379,9 +397,24 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int b = blockIdx.z, h = blockIdx.y;
+  // 1-D grid over (query tile, head, batch). Query tile slowest, last tile first: under the causal
+  // mask the last tiles, which see the most key tiles, go first (longest first). Query tile fastest:
+  // the tiles of one head are dispatched together and share its K/V stream in cache.
+  const int64_t lin = blockIdx.x;
+  const int n_qt_all = (p.Nq + BQ - 1) / BQ;
+  int h, b, q0;
+  if (p.dq_block_slowest) {
+    const int64_t per_qt = (int64_t)p.Hq * p.B;
+    h = (int)(lin % p.Hq);
+    b = (int)((lin % per_qt) / p.Hq);
+    q0 = (n_qt_all - 1 - (int)(lin / per_qt)) * BQ;
+  } else {
+    const int64_t rest = lin / n_qt_all;
+    q0 = (int)(lin % n_qt_all) * BQ;
+    h = (int)(rest % p.Hq);
+    b = (int)(rest / p.Hq);
+  }
   const int kvh = h / p.group;
-  const int q0 = blockIdx.x * BQ;
   const int wq0 = q0 + 32 * wave;
   const int my_row = wq0 + (lane & 31);
   const bool row_ok = my_row < p.Nq;

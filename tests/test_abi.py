@@ -168,8 +168,8 @@ BWD_BAD = [
     ("null_dk", dict(dk=0), "FA_ERR_NULL"), ("null_do_stride", dict(dos=None), "FA_ERR_NULL"),
     ("dtype", dict(dtype=3), "FA_ERR_DTYPE"), ("head_dim", dict(D=96), "FA_ERR_HEAD_DIM"),
     ("gqa", dict(Hq=3, Hkv=2), "FA_ERR_GQA"), ("zero_nkv", dict(Nkv=0), "FA_ERR_SHAPE"),
-    ("batch_over_grid", dict(B=70000, qs=(0, 8192, 64, 1), ks=(0, 8192, 64, 1), vs=(0, 8192, 64, 1),
-                              os=(0, 8192, 64, 1), dos=(0, 8192, 64, 1)), "FA_ERR_SHAPE"),
+    ("grid_over_2p31", dict(B=300, Nq=1 << 30, Nkv=1 << 30, qs=(0, 0, 64, 1), ks=(0, 0, 64, 1), vs=(0, 0, 64, 1),
+                            os=(0, 0, 64, 1), dos=(0, 0, 64, 1)), "FA_ERR_SHAPE"),
     ("dq_d_stride", dict(dqs=(16384, 8192, 64, 2)), "FA_ERR_LAYOUT"),
     ("dk_zero_stride", dict(dks=(8192, 8192, 0, 1)), "FA_ERR_LAYOUT"),
     ("misaligned_dv", dict(dv=0x90008), "FA_ERR_LAYOUT"), ("misaligned_delta", dict(delta=0xA0002), "FA_ERR_LAYOUT"),
