@@ -29,6 +29,14 @@
 //    requirements).
 //  * D = 256 keeps eight 32-row accumulator blocks per query block, i.e. the two
 //    D128 halves of the Ascend notes (sections 1 and 7) each as four blocks.
+//  * Persistent grid: each workgroup loops over (batch, query head, query tile)
+//    items dealt by an XCD-aware schedule (fa_layout.h), longest first under the
+//    causal mask.
+//  * Two more instances of the same kernel: WINDOW (a sliding-window mask, row i
+//    sees keys i - left .. i + right; only the band's key tiles are visited) and
+//    VARLEN (packed sequences addressed through cu_seqlens offsets, each with its
+//    own length), the masking variants "Write Triton Attention Kernel" lists
+//    among its inputs (items 3 and 6).
 #pragma once
 
 #include <hip/hip_runtime.h>
