@@ -12,8 +12,10 @@ Prints ONE JSON line. Extra objects:
                   products of the backward (10*B*Hq*Nq*Nkv*D, halved for the causal mask).
   roofline      - the dominant launch (the non-causal forward): algorithmic FLOP / its average
                   duration from HIP events on the launch stream, against the dense bf16 MFMA peak;
-                  `traffic` is the HBM bytes per launch from committed rocprofv3 counters when they
-                  were taken on the current kernel sources, else null.
+                  `traffic` is the HBM bytes per launch and `sclk_mhz` the shader clock during the
+                  kernel (with `frac_clock_adjusted`, the fraction of the peak at that clock), both
+                  from committed rocprofv3 counters when they were taken on the current kernel
+                  sources, else null.
   cpu_baseline  - the float64 CPU oracle timed on this host's cores on the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -57,7 +59,9 @@ def algorithmic_bytes(w) -> int:
     return e * (2 * w.B * w.Hq * w.Nq * w.D + 2 * w.B * w.Hkv * w.Nkv * w.D) + 4 * w.B * w.Hq * w.Nq
 
 
-def load_traffic(workload: str, mode: str):
+def load_profile(workload: str, mode: str, key: str):
+    """A per-launch figure from the committed rocprofv3 counters, if they were taken on the current
+    kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -68,7 +72,7 @@ def load_traffic(workload: str, mode: str):
     if rec.get("kernel_sha") != kernel_sha():
         return None
     m = rec.get("modes", {}).get(mode)
-    return None if m is None else m.get("hbm_bytes_per_launch")
+    return None if m is None else m.get(key)
 
 
 def cpu_baseline(w, q, k, v, outs):
@@ -211,8 +215,14 @@ def main():
     dominant = max(modes, key=lambda c: per_mode_ms[c])
     dom_ms = per_mode_ms[dominant] / args.steps
     achieved = flop(w, dominant) / (dom_ms / 1e3) / 1e12
+    sclk = load_profile(w.name, mode_name[dominant], "sclk_mhz")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name, mode_name[dominant]),
+                "frac": round(achieved / peak, 4),
+                "traffic": load_profile(w.name, mode_name[dominant], "hbm_bytes_per_launch"),
+                # the published peak is quoted at 2.4 GHz; the clock the kernel actually runs at comes
+                # from the committed GRBM_GUI_ACTIVE counters (profiles/)
+                "sclk_mhz": sclk,
+                "frac_clock_adjusted": round(achieved / (peak * sclk / 2400.0), 4) if sclk else None,
                 "kernel": f"fa_fwd_kernel<{w.dtype_name}, causal={dominant}, D={w.D}>",
                 "algorithmic_flop_per_launch": flop(w, dominant),
                 "algorithmic_bytes_per_launch": algorithmic_bytes(w)}
