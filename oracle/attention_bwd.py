@@ -24,6 +24,10 @@ which are the sums of their per-head terms (the chain rule through the shared
 tensor); Delta uses the exact O, not a rounded one. No tiling, recomputation
 order or 16-bit rounding of the kernel is emulated.
 
+With a sliding window (row i sees keys i - left .. i + right, as in the forward
+oracle) P is the softmax over the window; a row whose window holds no key has
+P = 0, so its dQ row is zero and it adds nothing to dK or dV.
+
 Query rows are processed in chunks purely to bound memory; the per-row terms
 are independent and dK, dV are sums over rows.
 """
@@ -44,19 +48,30 @@ def _f64(x) -> np.ndarray:
     return a
 
 
-def _softmax_rows(qh, kh, r, causal, scale):
+def _softmax_rows(qh, kh, r, causal, scale, window=None):
     """P for query rows r of one head: softmax of the scaled scores over the visible keys."""
     s = scale * (qh[r] @ kh.T)
+    key_pos = np.arange(kh.shape[0])
     if causal:
-        key_pos = np.arange(kh.shape[0])
         s = np.where(key_pos[None, :] <= r[:, None], s, -np.inf)  # top-left causal key set
+    if window is not None:
+        left, right = window
+        if left is not None:
+            s = np.where(key_pos[None, :] >= r[:, None] - left, s, -np.inf)
+        if right is not None:
+            s = np.where(key_pos[None, :] <= r[:, None] + right, s, -np.inf)
+    empty = np.all(s == -np.inf, axis=1)                # a window can leave a row without keys
+    s[empty] = 0.0
     m = np.max(s, axis=1, keepdims=True)
     e = np.exp(s - m)
-    return e / np.sum(e, axis=1, keepdims=True)
+    e[empty] = 0.0
+    z = np.sum(e, axis=1, keepdims=True)
+    z[empty] = 1.0
+    return e / z
 
 
 def head_bwd_ref(qh, kh, vh, doh, *, causal: bool, scale: float,
-                 row_chunk: int = 512) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                 row_chunk: int = 512, window=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Gradients of one query head against the key/value head it reads.
 
     qh: (Nq, D), kh: (Nkv, D), vh: (Nkv, Dv), doh: (Nq, Dv).
@@ -69,7 +84,7 @@ def head_bwd_ref(qh, kh, vh, doh, *, causal: bool, scale: float,
     rows = np.arange(qh.shape[0])
     for start in range(0, rows.shape[0], row_chunk):
         r = rows[start:start + row_chunk]
-        p = _softmax_rows(qh, kh, r, causal, scale)      # recomputed probabilities
+        p = _softmax_rows(qh, kh, r, causal, scale, window)  # recomputed probabilities
         o = p @ vh                                       # exact forward output of these rows
         delta = np.sum(o * doh[r], axis=1)               # Delta = rowsum(O * dO)
         dp = doh[r] @ vh.T                               # dP = dO V^T
@@ -81,7 +96,7 @@ def head_bwd_ref(qh, kh, vh, doh, *, causal: bool, scale: float,
 
 
 def attention_bwd_ref(q, k, v, do, *, causal: bool, scale: Optional[float] = None,
-                      row_chunk: int = 512) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                      row_chunk: int = 512, window=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Full attention backward in float64.
 
     q: (B, Hq, Nq, D); k: (B, Hkv, Nkv, D); v: (B, Hkv, Nkv, Dv); do: (B, Hq, Nq, Dv).
@@ -106,7 +121,7 @@ def attention_bwd_ref(q, k, v, do, *, causal: bool, scale: Optional[float] = Non
         for h in range(Hq):
             kvh = h // group
             dq[b, h], dkh, dvh = head_bwd_ref(q[b, h], k[b, kvh], v[b, kvh], do[b, h], causal=causal,
-                                              scale=scale, row_chunk=row_chunk)
+                                              scale=scale, row_chunk=row_chunk, window=window)
             dk[b, kvh] += dkh   # every query head of the group adds its terms
             dv[b, kvh] += dvh
     return dq, dk, dv

@@ -161,6 +161,46 @@ def pin_bwd_dq_rows_agree(mod):
         _close(mod.dq_rows(q, k, v, do, 1, 3, rows, causal=causal, scale=0.3), dq[1, 3, rows], what="dq rows")
 
 
+# 11. Sliding windows: finite differences through the windowed forward oracle, and torch float64
+#     autograd through SDPA with an explicit boolean band mask (windows that leave no row empty).
+def pin_bwd_window(mod):
+    q, k, v, do = _inputs(111, 1, 2, 1, 6, 7, 3)
+    for left, right in ((1, 0), (0, 2), (2, None)):
+        dq, dk, dv = mod.attention_bwd_ref(q, k, v, do, causal=False, scale=0.6, window=(left, right))
+
+        def loss(q_, k_, v_):
+            o, _ = fwd_oracle.attention_ref(q_, k_, v_, causal=False, scale=0.6, window=(left, right))
+            return float(np.sum(o * do))
+
+        h = 1e-5
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                ap = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                am = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                num[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+            _close(g, num, tol=1e-7, what=f"window ({left},{right}) finite differences d{name}")
+    q, k, v, do = _inputs(112, 1, 4, 2, 20, 20, 8)
+    i = np.arange(20)[:, None]
+    j = np.arange(20)[None, :]
+    band = (j >= i - 5) & (j <= i + 2)
+    dq, dk, dv = mod.attention_bwd_ref(q, k, v, do, causal=False, scale=0.35, window=(5, 2))
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(band), scale=0.35,
+                                                         enable_gqa=True)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    _close(dq, tq.grad.numpy(), tol=1e-12, what="window autograd dq")
+    _close(dk, tk.grad.numpy(), tol=1e-12, what="window autograd dk")
+    _close(dv, tv.grad.numpy(), tol=1e-12, what="window autograd dv")
+    # a row whose window holds no key has zero gradients everywhere it could reach
+    q, k, v, do = _inputs(113, 1, 1, 1, 8, 5, 3)
+    dq, dk, dv = mod.attention_bwd_ref(q, k, v, do, causal=False, scale=0.5, window=(0, 0))
+    assert np.all(dq[0, 0, 5:] == 0.0), "rows without keys have dQ = 0"
+
+
 ALL_BWD_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_torch_autograd,
@@ -172,4 +212,5 @@ ALL_BWD_PINS = [
     pin_bwd_scale_moves_to_q,
     pin_bwd_causal_last_key,
     pin_bwd_dq_rows_agree,
+    pin_bwd_window,
 ]

@@ -28,10 +28,12 @@ MUTANTS = [
     ("dq_keys_reversed", "dq[r] = ds @ kh", "dq[r] = ds @ kh[::-1]"),
     ("dp_values_reversed", "dp = doh[r] @ vh.T", "dp = doh[r] @ vh[::-1].T"),
     ("causal_strict", "key_pos[None, :] <= r[:, None]", "key_pos[None, :] < r[:, None]"),
-    ("causal_ignored", "if causal:\n        key_pos", "if False:\n        key_pos"),
+    ("causal_ignored", "if causal:\n        s = np.where", "if False:\n        s = np.where"),
     ("group_not_summed", "dk[b, kvh] += dkh", "dk[b, kvh] = dkh"),
     ("gqa_modulo", "kvh = h // group", "kvh = h % Hkv"),
-    ("no_normalisation", "return e / np.sum(e, axis=1, keepdims=True)", "return e"),
+    ("no_normalisation", "return e / z", "return e"),
+    ("window_left_off_by_one", "r[:, None] - left, s", "r[:, None] - left - 1, s"),
+    ("window_right_ignored", "if right is not None:\n            s", "if False:\n            s"),
     ("rows_dq_scale_dropped", "ds = scale * p * (doh @ vh.T - delta[:, None])", "ds = p * (doh @ vh.T - delta[:, None])"),
 ]
 
