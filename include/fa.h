@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 /* Element types of Q, K, V and O (all four share one type). */
 #define FA_DTYPE_F16 0
@@ -167,6 +167,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const int64_t o_stride[4], const int64_t do_stride[4], const int64_t dq_stride[4],
            const int64_t dk_stride[4], const int64_t dv_stride[4],
            float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_bwd_window - fa_bwd for a forward run by fa_fwd_window: the same arguments, with the
+ * window (window_left, window_right; -1 = unbounded side) in place of the causal flag. P is the
+ * softmax over each row's window; a row whose window holds no key (LSE = -inf) gets dQ = 0 and
+ * adds nothing to dK or dV. Validation as fa_bwd plus the window rules of fa_fwd_window.
+ */
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* delta,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                  const int64_t q_stride[4], const int64_t k_stride[4], const int64_t v_stride[4],
+                  const int64_t o_stride[4], const int64_t do_stride[4], const int64_t dq_stride[4],
+                  const int64_t dk_stride[4], const int64_t dv_stride[4],
+                  float scale, int64_t window_left, int64_t window_right, int dtype, void* stream);
 
 /* Launch plan of fa_fwd for a shape, computed on the host without any HIP call. */
 typedef struct fa_plan {

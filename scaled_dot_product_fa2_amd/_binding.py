@@ -54,6 +54,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                            i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f32, i32, i32, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                  i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f32, i64, i64, i32, vp]
+    lib.fa_bwd_window.restype = i32
     lib.fa_fwd_plan.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(_Plan)]
     lib.fa_fwd_plan.restype = i32
     lib.fa_tile_pairs.argtypes = [i64, i64, i64, i64, i32]
@@ -176,13 +179,14 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = 
 def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
            dout: torch.Tensor, *, causal: bool = False, scale: Optional[float] = None,
            dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-           delta: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None
-           ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+           delta: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None,
+           window: Optional[Tuple[int, int]] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Attention backward: returns (dq, dk, dv) for the forward (o, lse) = fa_fwd(q, k, v).
 
     dout is the gradient of the loss with respect to o (same shape and dtype). dq, dk, dv (shaped
     like q, k, v) and the float32 workspace ``delta`` (contiguous (B, Hq, Nq)) are allocated when
-    not passed. Same dtype, stride and alignment rules as ``fa_fwd``.
+    not passed. Same dtype, stride and alignment rules as ``fa_fwd``. ``window=(left, right)``
+    runs the backward of ``fa_fwd_window`` (then ``causal`` must be False).
     """
     if not all(t.is_cuda for t in (q, k, v, o, lse, dout)):
         raise ValueError("all tensors must be on the GPU")
@@ -208,12 +212,17 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
         raise ValueError("delta must be a contiguous float32 (B, Hq, Nq) tensor")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    code = load_library().fa_bwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-        B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(o), _strides(dout),
-        _strides(dq), _strides(dk), _strides(dv), float(scale), int(bool(causal)), _DTYPES[q.dtype],
-        ctypes.c_void_p(stream.cuda_stream))
+    common = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+              B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(o), _strides(dout),
+              _strides(dq), _strides(dk), _strides(dv), float(scale))
+    if window is None:
+        code = load_library().fa_bwd(*common, int(bool(causal)), _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream))
+    else:
+        if causal:
+            raise ValueError("pass either causal or window, not both (the causal mask is window (-1, 0))")
+        code = load_library().fa_bwd_window(*common, int(window[0]), int(window[1]), _DTYPES[q.dtype],
+                                            ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return dq, dk, dv
 

@@ -195,7 +195,7 @@ struct BwdCfgFor {
 };
 
 
-template <typename T, bool CAUSAL, int D>
+template <typename T, bool CAUSAL, int D, bool WINDOW = false>
 int launch_bwd(fa::BwdParams p, hipStream_t stream) {
   typedef typename BwdCfgFor<D>::dkdv CK;
   typedef typename BwdCfgFor<D>::dq CQ;
@@ -213,30 +213,30 @@ int launch_bwd(fa::BwdParams p, hipStream_t stream) {
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   const dim3 kv_grid((unsigned)((int64_t)((p.Nkv + CK::BW - 1) / CK::BW) * p.Hkv * p.B));
   if constexpr (BwdCfgFor<D>::SPLIT_KV) {
-    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyV>), kv_grid, dim3(CK::THREADS), 0,
+    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyV, WINDOW>), kv_grid, dim3(CK::THREADS), 0,
                        stream, p);
     if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyK>), kv_grid, dim3(CK::THREADS), 0,
+    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyK, WINDOW>), kv_grid, dim3(CK::THREADS), 0,
                        stream, p);
   } else {
-    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdBoth>), kv_grid, dim3(CK::THREADS), 0,
+    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdBoth, WINDOW>), kv_grid, dim3(CK::THREADS), 0,
                        stream, p);
   }
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<T, CAUSAL, CQ>),
+  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<T, CAUSAL, CQ, WINDOW>),
                      dim3((unsigned)((int64_t)((p.Nq + CQ::BW - 1) / CQ::BW) * p.Hq * p.B)),
                      dim3(CQ::THREADS), 0, stream, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, bool WINDOW = false>
 int launch_bwd_d(int64_t D, const fa::BwdParams& p, hipStream_t stream) {
   switch (D) {
-    case 16: return launch_bwd<T, CAUSAL, 16>(p, stream);
-    case 32: return launch_bwd<T, CAUSAL, 32>(p, stream);
-    case 64: return launch_bwd<T, CAUSAL, 64>(p, stream);
-    case 128: return launch_bwd<T, CAUSAL, 128>(p, stream);
-    case 256: return launch_bwd<T, CAUSAL, 256>(p, stream);
+    case 16: return launch_bwd<T, CAUSAL, 16, WINDOW>(p, stream);
+    case 32: return launch_bwd<T, CAUSAL, 32, WINDOW>(p, stream);
+    case 64: return launch_bwd<T, CAUSAL, 64, WINDOW>(p, stream);
+    case 128: return launch_bwd<T, CAUSAL, 128, WINDOW>(p, stream);
+    case 256: return launch_bwd<T, CAUSAL, 256, WINDOW>(p, stream);
     default: return FA_ERR_HEAD_DIM;
   }
 }
@@ -370,12 +370,13 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   return cz ? launch_d<_Float16, true, false, true>(D, p, grid, s) : launch_d<_Float16, false, false, true>(D, p, grid, s);
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-           void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
-           int64_t Nkv, int64_t D, const int64_t q_stride[4], const int64_t k_stride[4],
-           const int64_t v_stride[4], const int64_t o_stride[4], const int64_t do_stride[4],
-           const int64_t dq_stride[4], const int64_t dk_stride[4], const int64_t dv_stride[4], float scale,
-           int causal, int dtype, void* stream) {
+static int bwd_entry(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t Hq,
+                     int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, const int64_t* q_stride,
+                     const int64_t* k_stride, const int64_t* v_stride, const int64_t* o_stride,
+                     const int64_t* do_stride, const int64_t* dq_stride, const int64_t* dk_stride,
+                     const int64_t* dv_stride, float scale, int causal, bool window, int64_t window_left,
+                     int64_t window_right, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta || !q_stride || !k_stride ||
       !v_stride || !o_stride || !do_stride || !dq_stride || !dk_stride || !dv_stride)
     return FA_ERR_NULL;
@@ -424,12 +425,44 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.group = (int32_t)(Hq / Hkv);
   p.c = (float)((double)scale * 1.4426950408889634074);
   p.scale = scale;
+  p.win_left = (int32_t)Nq;
+  p.win_right = (int32_t)Nkv;
+  if (window) {
+    if (window_left < -1 || window_right < -1) return FA_ERR_SHAPE;
+    if (Nq > kMaxWindowSeq || Nkv > kMaxWindowSeq) return FA_ERR_SHAPE;
+    p.win_left = (int32_t)(window_left < 0 || window_left > Nq ? Nq : window_left);
+    p.win_right = (int32_t)(window_right < 0 || window_right > Nkv ? Nkv : window_right);
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool cz = causal != 0;
+  if (window) return dtype == FA_DTYPE_BF16 ? launch_bwd_d<__bf16, false, true>(D, p, s)
+                                            : launch_bwd_d<_Float16, false, true>(D, p, s);
   if (dtype == FA_DTYPE_BF16)
     return cz ? launch_bwd_d<__bf16, true>(D, p, s) : launch_bwd_d<__bf16, false>(D, p, s);
   return cz ? launch_bwd_d<_Float16, true>(D, p, s) : launch_bwd_d<_Float16, false>(D, p, s);
+}
+
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+           int64_t Nkv, int64_t D, const int64_t q_stride[4], const int64_t k_stride[4],
+           const int64_t v_stride[4], const int64_t o_stride[4], const int64_t do_stride[4],
+           const int64_t dq_stride[4], const int64_t dk_stride[4], const int64_t dv_stride[4], float scale,
+           int causal, int dtype, void* stream) {
+  return bwd_entry(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride,
+                   o_stride, do_stride, dq_stride, dk_stride, dv_stride, scale, causal, false, -1, -1, dtype, stream);
+}
+
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                  int64_t Nkv, int64_t D, const int64_t q_stride[4], const int64_t k_stride[4],
+                  const int64_t v_stride[4], const int64_t o_stride[4], const int64_t do_stride[4],
+                  const int64_t dq_stride[4], const int64_t dk_stride[4], const int64_t dv_stride[4], float scale,
+                  int64_t window_left, int64_t window_right, int dtype, void* stream) {
+  return bwd_entry(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride,
+                   o_stride, do_stride, dq_stride, dk_stride, dv_stride, scale, 0, true, window_left, window_right,
+                   dtype, stream);
 }
 
 }  // extern "C"

@@ -60,6 +60,8 @@ struct BwdParams {
   // order of the 1-D gradient grids: nonzero = row block slowest (longest first under the causal
   // mask; L2 sharing between the blocks of a head when the grid is about one wave of workgroups)
   int32_t dkdv_block_slowest, dq_block_slowest;
+  // sliding window (the WINDOW instances only): row i sees keys i - win_left .. i + win_right
+  int32_t win_left, win_right;
 };
 
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -69,6 +71,11 @@ constexpr float kLog2e = 1.44269504088896340736f;
 #define BWD_LEAD 3
 #endif
 constexpr int kBwdLead = BWD_LEAD;
+// The dQ kernel's score loop at D >= 128 under a mask holds the mask's row bounds as well; one
+// fragment less read-ahead there keeps it inside the register file.
+#ifndef BWD_DQ_MASKED_LEAD
+#define BWD_DQ_MASKED_LEAD 2
+#endif
 
 // Compile-time part of the row-fragment read of rows 32*qb + (lane % 32), chunk 2*s + lane/32, of a
 // tile in the transposing (unswizzled) layout; the per-lane part depends on s only through its parity.
@@ -122,7 +129,7 @@ struct BwdCfg {
 // kBwdOnlyV / kBwdOnlyK (two launches, S recomputed in each, to fit wide heads in registers).
 constexpr int kBwdBoth = 0, kBwdOnlyV = 1, kBwdOnlyK = 2;
 
-template <typename T, bool CAUSAL, class Cfg, int PART>
+template <typename T, bool CAUSAL, class Cfg, int PART, bool WINDOW = false>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
     fa_bwd_dkdv_kernel(const BwdParams p) {
@@ -192,8 +199,15 @@ __global__ void __launch_bounds__(Cfg::THREADS)
 
   // Work list: (query head of the group, query tile), tiles that can see one of the keys only.
   const int n_qt = (p.Nq + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? (k0 / BQ < n_qt ? k0 / BQ : n_qt) : 0;
-  const int per_head = n_qt - qt0;
+  int qt0 = CAUSAL ? (k0 / BQ < n_qt ? k0 / BQ : n_qt) : 0, qt_end = n_qt;
+  if (WINDOW) {
+    // rows that see one of the workgroup's keys: key - win_right <= row <= key + win_left
+    const int first = max(0, k0 - p.win_right);
+    const int last = min(p.Nq - 1, k0 + BK - 1 + p.win_left);
+    qt0 = min(first / BQ, n_qt);
+    qt_end = first > last ? qt0 : last / BQ + 1;
+  }
+  const int per_head = qt_end - qt0;
   const int n_work = p.group * per_head;
   const int q_stride = (int)(p.q_sn * 2), o_stride = (int)(p.do_sn * 2);
   const int q_dma_off = (int)dma_lane_offset<D, true>(lane, q_stride);
@@ -254,6 +268,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       const int qrow0 = q0 + 32 * qb;
       // every query row of the block is before the wave's first key: nothing visible
       if (CAUSAL && qrow0 + 31 < kw0) continue;
+      // with a window: the block's rows are all outside every key's window
+      if (WINDOW && (qrow0 + 31 < kw0 - p.win_right || qrow0 > kw0 + 31 + p.win_left)) continue;
       if (qrow0 >= p.Nq) continue;
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
       {
@@ -292,6 +308,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           const int r = 4 * g + e;
           float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c, -lv[e] * kLog2e));
           if (CAUSAL && my_key > qrow0 + m0 + e) pv = 0.f;
+          if (WINDOW && (my_key > qrow0 + m0 + e + p.win_right || my_key < qrow0 + m0 + e - p.win_left)) pv = 0.f;
           const float ds = pv * (dp_acc[r] - dv4[e]);
           pf[r >> 3][r & 7] = (T)pv;
           sf[r >> 3][r & 7] = (T)ds;
@@ -373,7 +390,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
 
 // ------------------------------------------------------------------------------------------------
 // dQ. Grid: ceil(Nq / BW) * Hq * B workgroups (1-D).
-template <typename T, bool CAUSAL, class Cfg>
+template <typename T, bool CAUSAL, class Cfg, bool WINDOW = false>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
     fa_bwd_dq_kernel(const BwdParams p) {
@@ -443,7 +460,16 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const int k_stride = (int)(p.k_sn * 2), v_stride = (int)(p.v_sn * 2);
   const int k_dma_off = (int)dma_lane_offset<D, true>(lane, k_stride);
   const int v_dma_off = (int)dma_lane_offset<D, false>(lane, v_stride);
-  const int n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
+  // key tiles this workgroup visits: [t0, t0 + n_tiles)
+  int t0 = 0, n_tiles;
+  if (WINDOW) {
+    const int first = max(0, q0 - p.win_left);
+    const int last = min(p.Nkv - 1, min(q0 + BQ, p.Nq) - 1 + p.win_right);
+    t0 = first / BKV;
+    n_tiles = first > last ? 0 : last / BKV + 1 - t0;
+  } else {
+    n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
+  }
   const int wq_last = wq0 + 31;
   const float c = p.c;
 
@@ -460,7 +486,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     constexpr int S = decltype(stage_c)::value;
     lds_char_t* const kt = (lds_char_t*)(S == 0 ? k_st0_raw : k_st1_raw);
     lds_char_t* const vt = (lds_char_t*)(S == 0 ? v_st0_raw : v_st1_raw);
-    const int kpos = j * BKV;
+    const int kpos = (t0 + j) * BKV;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (j + 1 < n_tiles) {
@@ -470,6 +496,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       dma_tile<D, BKV, NW>(vn, vbase, v_stride, kpos + BKV, p.Nkv, wave_u, v_dma_off);
     }
     if (CAUSAL && kpos > wq_last) return;
+    if (WINDOW && (kpos > wq_last + p.win_right || kpos + BKV - 1 < wq0 - p.win_left)) return;
     f32x16 st[NKB], dpt[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -492,7 +519,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           st[kb] = Elem<T>::mfma(ka[s][kb], qf[s], st[kb]);
           dpt[kb] = Elem<T>::mfma(va[s][kb], of[s], dpt[kb]);
         }
-      constexpr int LEAD = kBwdLead < NS ? kBwdLead : NS;
+      constexpr int LEAD_S = D >= 128 && (CAUSAL || WINDOW) ? BWD_DQ_MASKED_LEAD : kBwdLead;
+      constexpr int LEAD = LEAD_S < NS ? LEAD_S : NS;
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * NKB * LEAD, 0);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -504,13 +532,15 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     const int base = kpos + 4 * half;
     int limit = p.Nkv - 1 - base;
     if (CAUSAL) limit = min(limit, my_row - base);
+    if (WINDOW) limit = min(limit, my_row + p.win_right - base);
+    const int lower = WINDOW ? my_row - p.win_left - base : -1;  // keys below the window
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int koff = 32 * kb + 8 * (r >> 2) + (r & 3);
         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c, -lse2));
-        pv = koff > limit ? 0.f : pv;
+        pv = (koff > limit || koff < lower) ? 0.f : pv;
         st[kb][r] = pv * (dpt[kb][r] - dlt);  // dS^T / scale
       }
     vec8 sfr[NKS];
@@ -547,8 +577,10 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     }
   };
 
-  dma_tile<D, BKV, NW>((lds_char_t*)k_st0_raw, kbase, k_stride, 0, p.Nkv, wave_u, k_dma_off);
-  dma_tile<D, BKV, NW>((lds_char_t*)v_st0_raw, vbase, v_stride, 0, p.Nkv, wave_u, v_dma_off);
+  if (n_tiles > 0) {
+    dma_tile<D, BKV, NW>((lds_char_t*)k_st0_raw, kbase, k_stride, t0 * BKV, p.Nkv, wave_u, k_dma_off);
+    dma_tile<D, BKV, NW>((lds_char_t*)v_st0_raw, vbase, v_stride, t0 * BKV, p.Nkv, wave_u, v_dma_off);
+  }
   int j = 0;
   for (; j + 1 < n_tiles; j += 2) {
     step(IC<0>(), j);

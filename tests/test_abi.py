@@ -183,6 +183,28 @@ def test_bwd_validation_rejects(name, over, code):
     assert _bwd_call(**over) == D_[code]
 
 
+def _bwd_win_call(left, right, **over):
+    a = dict(BWD_VALID)
+    a.update(over)
+    lib = _lib()
+    st = [(_st(*a[n]) if a[n] else None) for n in ("qs", "ks", "vs", "os", "dos", "dqs", "dks", "dvs")]
+    return lib.fa_bwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                             a["delta"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["D"], *st, a["scale"], left,
+                             right, a["dtype"], None)
+
+
+@pytest.mark.parametrize("left,right,over,code", [
+    (-2, 0, {}, "FA_ERR_SHAPE"), (3, -7, {}, "FA_ERR_SHAPE"),
+    (4, 4, dict(Nkv=(1 << 30) + 1, ks=(0, 64 * ((1 << 30) + 1), 64, 1), vs=(0, 64 * ((1 << 30) + 1), 64, 1),
+                dks=(0, 64 * ((1 << 30) + 1), 64, 1), dvs=(0, 64 * ((1 << 30) + 1), 64, 1)), "FA_ERR_SHAPE"),
+    (4, 4, dict(D=80), "FA_ERR_HEAD_DIM"), (4, 4, dict(dq=0), "FA_ERR_NULL"), (4, 4, dict(lse=0x50001), "FA_ERR_LAYOUT"),
+    (4, 4, dict(scale=-1.0), "FA_ERR_SCALE"), (4, 4, dict(dtype=7), "FA_ERR_DTYPE"),
+], ids=["left_below_minus1", "right_below_minus1", "nkv_over_2p30", "head_dim", "null_dq", "misaligned_lse",
+        "scale", "dtype"])
+def test_bwd_window_validation_rejects(left, right, over, code):
+    assert _bwd_win_call(left, right, **over) == D_[code]
+
+
 def _win_call(left, right, **over):
     a = dict(VALID)
     a.update(over)
