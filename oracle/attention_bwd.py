@@ -28,6 +28,11 @@ With a sliding window (row i sees keys i - left .. i + right, as in the forward
 oracle) P is the softmax over the window; a row whose window holds no key has
 P = 0, so its dQ row is zero and it adds nothing to dK or dV.
 
+Packed variable-length sequences (the CSR layout of the forward oracle's
+attention_varlen_ref) are independent attention problems, so each sequence's
+gradients are the dense backward of that sequence alone; a sequence with no
+query rows or no keys has zero gradients on its tokens.
+
 Query rows are processed in chunks purely to bound memory; the per-row terms
 are independent and dK, dV are sums over rows.
 """
@@ -38,7 +43,7 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["attention_bwd_ref", "head_bwd_ref", "dq_rows"]
+__all__ = ["attention_bwd_ref", "head_bwd_ref", "dq_rows", "attention_varlen_bwd_ref"]
 
 
 def _f64(x) -> np.ndarray:
@@ -143,3 +148,35 @@ def dq_rows(q, k, v, do, b: int, h: int, rows: Sequence[int], *, causal: bool,
     delta = np.sum((p @ vh) * doh, axis=1)
     ds = scale * p * (doh @ vh.T - delta[:, None])
     return ds @ kh
+
+
+def attention_varlen_bwd_ref(q, k, v, do, cu_seqlens_q, cu_seqlens_k, *, causal: bool,
+                             scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Backward over packed variable-length sequences, in float64.
+
+    q: (total_q, Hq, D), k: (total_k, Hkv, D), v: (total_k, Hkv, Dv), do: (total_q, Hq, Dv), token-major;
+    sequence b owns query tokens cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 and key tokens
+    cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1, positions counted from its own start. Returns dq, dk, dv
+    shaped like q, k, v.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    if len(cq) != len(ck) or cq[0] != 0 or ck[0] != 0 or cq[-1] != q.shape[0] or ck[-1] != k.shape[0]:
+        raise ValueError("cu_seqlens must start at 0 and end at the token counts, one entry per sequence + 1")
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[2])
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 <= q0 or k1 <= k0:
+            continue                      # nothing attends, nothing is attended: zero gradients
+        gq, gk, gv = attention_bwd_ref(q[q0:q1].transpose(1, 0, 2)[None], k[k0:k1].transpose(1, 0, 2)[None],
+                                       v[k0:k1].transpose(1, 0, 2)[None], do[q0:q1].transpose(1, 0, 2)[None],
+                                       causal=causal, scale=scale)
+        dq[q0:q1] = gq[0].transpose(1, 0, 2)
+        dk[k0:k1] = gk[0].transpose(1, 0, 2)
+        dv[k0:k1] = gv[0].transpose(1, 0, 2)
+    return dq, dk, dv

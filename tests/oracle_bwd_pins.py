@@ -1,7 +1,7 @@
 """Checks that pin the float64 backward oracle to facts that do not come from it.
 
-Each pin takes a backward-oracle module (anything exposing ``attention_bwd_ref``
-and ``dq_rows``) and raises AssertionError when the module disagrees with the
+Each pin takes a backward-oracle module (anything exposing ``attention_bwd_ref``,
+``attention_varlen_bwd_ref`` and ``dq_rows``) and raises AssertionError when the module disagrees with the
 fact it pins. They run against the real module in ``test_oracle_bwd.py`` and
 against deliberately broken copies of it there too.
 
@@ -201,6 +201,59 @@ def pin_bwd_window(mod):
     assert np.all(dq[0, 0, 5:] == 0.0), "rows without keys have dQ = 0"
 
 
+# 12. Packed variable-length sequences: finite differences through the (separately pinned) packed
+#     forward oracle, torch float64 autograd through SDPA over all the packed tokens with a
+#     block-diagonal (per-sequence, optionally causal) boolean mask, and zero gradients on the
+#     tokens of sequences without queries or without keys.
+def pin_bwd_varlen(mod):
+    rng = _rng(121)
+    cu_q, cu_k = [0, 2, 2, 5, 6], [0, 3, 4, 6, 6]   # sequence 1 has no queries, sequence 3 no keys
+    q, k, v = rng.standard_normal((6, 2, 3)), rng.standard_normal((6, 1, 3)), rng.standard_normal((6, 1, 3))
+    do = rng.standard_normal((6, 2, 3))
+    for causal in (False, True):
+        dq, dk, dv = mod.attention_varlen_bwd_ref(q, k, v, do, cu_q, cu_k, causal=causal, scale=0.8)
+
+        def loss(q_, k_, v_):
+            o, _ = fwd_oracle.attention_varlen_ref(q_, k_, v_, cu_q, cu_k, causal=causal, scale=0.8)
+            return float(np.sum(o * do))
+
+        h = 1e-5
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                ap = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                am = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                num[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+            _close(g, num, tol=1e-7, what=f"varlen causal={causal} finite differences d{name}")
+        assert np.all(dk[3] == 0.0) and np.all(dv[3] == 0.0), "keys of a sequence without queries"
+        assert np.all(dq[5] == 0.0), "queries of a sequence without keys"
+    # autograd: every sequence has queries and keys; group of 2
+    lens_q, lens_k = [5, 1, 9, 4], [7, 3, 9, 1]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lens_q)]), np.concatenate([[0], np.cumsum(lens_k)])
+    tq_, tk_ = int(cu_q[-1]), int(cu_k[-1])
+    q, k, v = rng.standard_normal((tq_, 4, 8)), rng.standard_normal((tk_, 2, 8)), rng.standard_normal((tk_, 2, 8))
+    do = rng.standard_normal((tq_, 4, 8))
+    seq_q = np.repeat(np.arange(4), lens_q)
+    seq_k = np.repeat(np.arange(4), lens_k)
+    pos_q = np.arange(tq_) - cu_q[seq_q]
+    pos_k = np.arange(tk_) - cu_k[seq_k]
+    for causal in (False, True):
+        mask = seq_q[:, None] == seq_k[None, :]
+        if causal:
+            mask &= pos_k[None, :] <= pos_q[:, None]
+        dq, dk, dv = mod.attention_varlen_bwd_ref(q, k, v, do, cu_q, cu_k, causal=causal, scale=0.4)
+        tq, tk, tv = (torch.tensor(x.transpose(1, 0, 2)[None], dtype=torch.float64, requires_grad=True)
+                      for x in (q, k, v))
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask), scale=0.4,
+                                                             enable_gqa=True)
+        o.backward(torch.tensor(do.transpose(1, 0, 2)[None], dtype=torch.float64))
+        for name, g, t in (("dq", dq, tq), ("dk", dk, tk), ("dv", dv, tv)):
+            _close(g, t.grad.numpy()[0].transpose(1, 0, 2), tol=1e-12, what=f"varlen causal={causal} autograd {name}")
+
+
 ALL_BWD_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_torch_autograd,
@@ -213,4 +266,5 @@ ALL_BWD_PINS = [
     pin_bwd_causal_last_key,
     pin_bwd_dq_rows_agree,
     pin_bwd_window,
+    pin_bwd_varlen,
 ]

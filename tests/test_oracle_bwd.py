@@ -35,6 +35,10 @@ MUTANTS = [
     ("window_left_off_by_one", "r[:, None] - left, s", "r[:, None] - left - 1, s"),
     ("window_right_ignored", "if right is not None:\n            s", "if False:\n            s"),
     ("rows_dq_scale_dropped", "ds = scale * p * (doh @ vh.T - delta[:, None])", "ds = p * (doh @ vh.T - delta[:, None])"),
+    ("varlen_keys_at_query_offsets", "k[k0:k1].transpose(1, 0, 2)[None],\n", "k[q0:q0 + k1 - k0].transpose(1, 0, 2)[None],\n"),
+    ("varlen_dk_not_written", "dk[k0:k1] = gk[0].transpose(1, 0, 2)", "pass"),
+    ("varlen_causal_dropped", "v[k0:k1].transpose(1, 0, 2)[None], do[q0:q1].transpose(1, 0, 2)[None],\n                                       causal=causal",
+     "v[k0:k1].transpose(1, 0, 2)[None], do[q0:q1].transpose(1, 0, 2)[None],\n                                       causal=False"),
 ]
 
 
@@ -61,3 +65,4 @@ def test_backward_pins_catch_mutant(name, find, replace):
 
 def test_exported():
     assert oracle.attention_bwd_ref is attention_bwd.attention_bwd_ref
+    assert oracle.attention_varlen_bwd_ref is attention_bwd.attention_varlen_bwd_ref
