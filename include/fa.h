@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 /* Element types of Q, K, V and O (all four share one type). */
 #define FA_DTYPE_F16 0
@@ -181,6 +181,30 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, co
                   const int64_t o_stride[4], const int64_t do_stride[4], const int64_t dq_stride[4],
                   const int64_t dk_stride[4], const int64_t dv_stride[4],
                   float scale, int64_t window_left, int64_t window_right, int dtype, void* stream);
+
+/*
+ * fa_bwd_varlen - the backward of fa_fwd_varlen (packed variable-length sequences, "Write Triton
+ * Attention Kernel", Inputs item 6): the tensors and offsets of that call plus
+ *
+ * dout       : dO, token-major (total_q, Hq, D) with strides do_stride (token, head, dim)
+ * dq         : (total_q, Hq, D), strides dq_stride; dk, dv: (total_k, Hkv, D), strides dk_stride, dv_stride
+ * lse        : fp32 (Hq, total_q) contiguous, as written by fa_fwd_varlen
+ * delta      : caller-provided fp32 workspace of Hq * total_q floats, overwritten, laid out like lse
+ *
+ * Each sequence's gradients depend on its own tokens only: dk and dv of a sequence with keys but no
+ * queries are zero, and dq of a sequence with queries but no keys is zero. Tokens outside every
+ * sequence (before cu_seqlens[0] or after cu_seqlens[B]) are not written. Validation as
+ * fa_fwd_varlen plus the output rules of fa_bwd; ceil(max_seqlen/128) * heads * B < 2^31.
+ */
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* delta,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t total_q, int64_t total_k,
+                  int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D,
+                  const int64_t q_stride[3], const int64_t k_stride[3], const int64_t v_stride[3],
+                  const int64_t o_stride[3], const int64_t do_stride[3], const int64_t dq_stride[3],
+                  const int64_t dk_stride[3], const int64_t dv_stride[3],
+                  float scale, int causal, int dtype, void* stream);
 
 /* Launch plan of fa_fwd for a shape, computed on the host without any HIP call. */
 typedef struct fa_plan {

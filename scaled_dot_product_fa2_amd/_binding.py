@@ -57,6 +57,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                   i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f32, i64, i64, i32, vp]
     lib.fa_bwd_window.restype = i32
+    i64_3 = ctypes.POINTER(ctypes.c_int64)
+    lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                  i64, i64_3, i64_3, i64_3, i64_3, i64_3, i64_3, i64_3, i64_3, f32, i32, i32, vp]
+    lib.fa_bwd_varlen.restype = i32
     lib.fa_fwd_plan.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(_Plan)]
     lib.fa_fwd_plan.restype = i32
     lib.fa_tile_pairs.argtypes = [i64, i64, i64, i64, i32]
@@ -308,3 +312,57 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
         ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return out, lse
+
+
+def fa_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                  dout: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
+                  max_seqlen_k: int, *, causal: bool = False, scale: Optional[float] = None,
+                  dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                  dv: Optional[torch.Tensor] = None, delta: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of ``fa_fwd_varlen``: returns (dq, dk, dv) shaped like q, k, v (token-major).
+
+    o and lse are that call's outputs ((total_q, Hq, D) and (Hq, total_q) float32), dout the gradient
+    of the loss with respect to o. The float32 workspace ``delta`` is (Hq, total_q).
+    """
+    if not all(t.is_cuda for t in (q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k)):
+        raise ValueError("all tensors must be on the GPU")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v, o, dout must share one dtype, float16 or bfloat16")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if not (cu_seqlens_q.is_contiguous() and cu_seqlens_k.is_contiguous()) or cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be contiguous with B + 1 entries each")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, _ = k.shape
+    if k.shape != (total_k, Hkv, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, o and dout")
+    if lse.shape != (Hq, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (Hq, total_q) tensor")
+    B = cu_seqlens_q.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError(f"{name} must match the shape, dtype and device of its input")
+    if delta is None:
+        delta = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    elif delta.shape != (Hq, total_q) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 (Hq, total_q) tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+
+    def st3(t):
+        return (ctypes.c_int64 * 3)(*t.stride())
+
+    code = load_library().fa_bwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+        dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv,
+        total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D, st3(q), st3(k), st3(v), st3(o), st3(dout),
+        st3(dq), st3(dk), st3(dv), float(scale), int(bool(causal)), _DTYPES[q.dtype],
+        ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return dq, dk, dv

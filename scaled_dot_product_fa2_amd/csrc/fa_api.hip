@@ -195,7 +195,7 @@ struct BwdCfgFor {
 };
 
 
-template <typename T, bool CAUSAL, int D, bool WINDOW = false>
+template <typename T, bool CAUSAL, int D, bool WINDOW = false, bool VARLEN = false>
 int launch_bwd(fa::BwdParams p, hipStream_t stream) {
   typedef typename BwdCfgFor<D>::dkdv CK;
   typedef typename BwdCfgFor<D>::dq CQ;
@@ -207,36 +207,45 @@ int launch_bwd(fa::BwdParams p, hipStream_t stream) {
   p.dkdv_block_slowest = CAUSAL || kv_wgs <= 2 * kNumCUs * (CK::WAVES_PER_SIMD * 4 / CK::NW);
   p.dq_block_slowest = CAUSAL || q_wgs <= 2 * kNumCUs * (CQ::WAVES_PER_SIMD * 4 / CQ::NW);
   constexpr int RPB = 256 / (D / 8);
-  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
+  // Delta is per token: packed sequences run it as one batch of total_q rows, which is the
+  // (Hq, total_q) layout of their logsumexp
+  fa::BwdParams pd = p;
+  if (VARLEN) {
+    pd.B = 1;
+    pd.Nq = p.total_q;
+    pd.o_sb = 0;
+    pd.do_sb = 0;
+  }
+  const int64_t rows = (int64_t)pd.B * pd.Hq * pd.Nq;
   hipLaunchKernelGGL((fa::fa_bwd_delta_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, p);
+                     stream, pd);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   const dim3 kv_grid((unsigned)((int64_t)((p.Nkv + CK::BW - 1) / CK::BW) * p.Hkv * p.B));
   if constexpr (BwdCfgFor<D>::SPLIT_KV) {
-    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyV, WINDOW>), kv_grid, dim3(CK::THREADS), 0,
-                       stream, p);
+    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyV, WINDOW, VARLEN>), kv_grid,
+                       dim3(CK::THREADS), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyK, WINDOW>), kv_grid, dim3(CK::THREADS), 0,
-                       stream, p);
+    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyK, WINDOW, VARLEN>), kv_grid,
+                       dim3(CK::THREADS), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdBoth, WINDOW>), kv_grid, dim3(CK::THREADS), 0,
-                       stream, p);
+    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdBoth, WINDOW, VARLEN>), kv_grid,
+                       dim3(CK::THREADS), 0, stream, p);
   }
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<T, CAUSAL, CQ, WINDOW>),
+  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<T, CAUSAL, CQ, WINDOW, VARLEN>),
                      dim3((unsigned)((int64_t)((p.Nq + CQ::BW - 1) / CQ::BW) * p.Hq * p.B)),
                      dim3(CQ::THREADS), 0, stream, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-template <typename T, bool CAUSAL, bool WINDOW = false>
+template <typename T, bool CAUSAL, bool WINDOW = false, bool VARLEN = false>
 int launch_bwd_d(int64_t D, const fa::BwdParams& p, hipStream_t stream) {
   switch (D) {
-    case 16: return launch_bwd<T, CAUSAL, 16, WINDOW>(p, stream);
-    case 32: return launch_bwd<T, CAUSAL, 32, WINDOW>(p, stream);
-    case 64: return launch_bwd<T, CAUSAL, 64, WINDOW>(p, stream);
-    case 128: return launch_bwd<T, CAUSAL, 128, WINDOW>(p, stream);
-    case 256: return launch_bwd<T, CAUSAL, 256, WINDOW>(p, stream);
+    case 16: return launch_bwd<T, CAUSAL, 16, WINDOW, VARLEN>(p, stream);
+    case 32: return launch_bwd<T, CAUSAL, 32, WINDOW, VARLEN>(p, stream);
+    case 64: return launch_bwd<T, CAUSAL, 64, WINDOW, VARLEN>(p, stream);
+    case 128: return launch_bwd<T, CAUSAL, 128, WINDOW, VARLEN>(p, stream);
+    case 256: return launch_bwd<T, CAUSAL, 256, WINDOW, VARLEN>(p, stream);
     default: return FA_ERR_HEAD_DIM;
   }
 }
@@ -370,19 +379,20 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   return cz ? launch_d<_Float16, true, false, true>(D, p, grid, s) : launch_d<_Float16, false, false, true>(D, p, grid, s);
 }
 
-static int bwd_entry(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                     const void* dout, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t Hq,
-                     int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, const int64_t* q_stride,
-                     const int64_t* k_stride, const int64_t* v_stride, const int64_t* o_stride,
-                     const int64_t* do_stride, const int64_t* dq_stride, const int64_t* dk_stride,
-                     const int64_t* dv_stride, float scale, int causal, bool window, int64_t window_left,
-                     int64_t window_right, int dtype, void* stream) {
+// Validation and parameters of a backward call over B batches of Nq query / Nkv key rows (dense
+// lengths; the window and the packed-sequence fields are filled in by the callers).
+static int prepare_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, const int64_t* q_stride,
+                       const int64_t* k_stride, const int64_t* v_stride, const int64_t* o_stride,
+                       const int64_t* do_stride, const int64_t* dq_stride, const int64_t* dk_stride,
+                       const int64_t* dv_stride, float scale, bool causal, int dtype, fa::BwdParams* out) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta || !q_stride || !k_stride ||
       !v_stride || !o_stride || !do_stride || !dq_stride || !dk_stride || !dv_stride)
     return FA_ERR_NULL;
   PlanInfo pi;
   int64_t n_qt = 0, grid = 0;
-  int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, causal != 0, &pi, &n_qt, &grid);
+  int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, causal, &pi, &n_qt, &grid);
   if (rc != FA_OK) return rc;
   // the gradient kernels use 1-D grids of (row block, head, batch) workgroups
   if (((Nkv + 127) / 128) * Hkv * B > kMaxDim || ((Nq + 127) / 128) * Hq * B > kMaxDim) return FA_ERR_SHAPE;
@@ -406,7 +416,7 @@ static int bwd_entry(const void* q, const void* k, const void* v, const void* o,
       !extent_ok(B, Hkv, Nkv, D, dk_stride) || !extent_ok(B, Hkv, Nkv, D, dv_stride))
     return FA_ERR_SHAPE;
 
-  fa::BwdParams p;
+  fa::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv; p.delta = delta;
   p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
@@ -427,6 +437,26 @@ static int bwd_entry(const void* q, const void* k, const void* v, const void* o,
   p.scale = scale;
   p.win_left = (int32_t)Nq;
   p.win_right = (int32_t)Nkv;
+  p.cu_q = nullptr;
+  p.cu_k = nullptr;
+  p.lse_sb = Hq * Nq;  // contiguous (B, Hq, Nq)
+  p.lse_sh = Nq;
+  *out = p;
+  return FA_OK;
+}
+
+static int bwd_entry(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t Hq,
+                     int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, const int64_t* q_stride,
+                     const int64_t* k_stride, const int64_t* v_stride, const int64_t* o_stride,
+                     const int64_t* do_stride, const int64_t* dq_stride, const int64_t* dk_stride,
+                     const int64_t* dv_stride, float scale, int causal, bool window, int64_t window_left,
+                     int64_t window_right, int dtype, void* stream) {
+  fa::BwdParams p;
+  const int rc = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nkv, D, q_stride, k_stride,
+                             v_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride, scale, causal != 0,
+                             dtype, &p);
+  if (rc != FA_OK) return rc;
   if (window) {
     if (window_left < -1 || window_right < -1) return FA_ERR_SHAPE;
     if (Nq > kMaxWindowSeq || Nkv > kMaxWindowSeq) return FA_ERR_SHAPE;
@@ -463,6 +493,63 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, co
   return bwd_entry(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride,
                    o_stride, do_stride, dq_stride, dk_stride, dv_stride, scale, 0, true, window_left, window_right,
                    dtype, stream);
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* delta, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, int64_t B, int64_t Hq, int64_t Hkv, int64_t total_q, int64_t total_k,
+                  int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D, const int64_t q_stride[3],
+                  const int64_t k_stride[3], const int64_t v_stride[3], const int64_t o_stride[3],
+                  const int64_t do_stride[3], const int64_t dq_stride[3], const int64_t dk_stride[3],
+                  const int64_t dv_stride[3], float scale, int causal, int dtype, void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k || !q_stride || !k_stride || !v_stride || !o_stride || !do_stride ||
+      !dq_stride || !dk_stride || !dv_stride)
+    return FA_ERR_NULL;
+  if (total_q < 1 || total_k < 1 || total_q > kMaxDim || total_k > kMaxDim) return FA_ERR_SHAPE;
+  if (max_seqlen_q < 1 || max_seqlen_k < 1 || max_seqlen_q > total_q || max_seqlen_k > total_k) return FA_ERR_SHAPE;
+  if (B < 1 || B + 1 > kMaxDim) return FA_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) != 0 || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u) != 0)
+    return FA_ERR_LAYOUT;
+  // token-major tensors, strides (token, head, dim): validated as one batch of all the tokens, then
+  // run as B sequences with batch stride 0 and the longest lengths
+  auto st4 = [](const int64_t* s3, int64_t* s4) {
+    s4[0] = 0;
+    s4[1] = s3[1];
+    s4[2] = s3[0];
+    s4[3] = s3[2];
+  };
+  int64_t qs[4], ks[4], vs[4], os[4], dos[4], dqs[4], dks[4], dvs[4];
+  st4(q_stride, qs);
+  st4(k_stride, ks);
+  st4(v_stride, vs);
+  st4(o_stride, os);
+  st4(do_stride, dos);
+  st4(dq_stride, dqs);
+  st4(dk_stride, dks);
+  st4(dv_stride, dvs);
+  fa::BwdParams p;
+  int rc = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, 1, Hq, Hkv, total_q, total_k, D, qs, ks, vs, os, dos,
+                       dqs, dks, dvs, scale, causal != 0, dtype, &p);
+  if (rc != FA_OK) return rc;
+  // the grids cover B sequences of the longest lengths
+  if (((max_seqlen_k + 127) / 128) * Hkv * B > kMaxDim || ((max_seqlen_q + 127) / 128) * Hq * B > kMaxDim)
+    return FA_ERR_SHAPE;
+  p.B = (int32_t)B;
+  p.Nq = (int32_t)max_seqlen_q;
+  p.Nkv = (int32_t)max_seqlen_k;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = (int32_t)total_q;
+  p.total_k = (int32_t)total_k;
+  p.lse_sb = 0;  // (Hq, total_q), as fa_fwd_varlen writes it
+  p.lse_sh = total_q;
+  p.win_left = (int32_t)max_seqlen_q;
+  p.win_right = (int32_t)max_seqlen_k;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool cz = causal != 0;
+  if (dtype == FA_DTYPE_BF16)
+    return cz ? launch_bwd_d<__bf16, true, false, true>(D, p, s) : launch_bwd_d<__bf16, false, false, true>(D, p, s);
+  return cz ? launch_bwd_d<_Float16, true, false, true>(D, p, s) : launch_bwd_d<_Float16, false, false, true>(D, p, s);
 }
 
 }  // extern "C"

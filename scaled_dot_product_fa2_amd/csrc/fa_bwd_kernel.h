@@ -17,6 +17,9 @@
 //    dQ accumulates in registers and is written once.
 // S and dP are recomputed in both gradient kernels (two extra products against
 // a scheme with atomic dQ updates) in exchange for deterministic results.
+// WINDOW and VARLEN instances of both gradient kernels mirror the forward's:
+// only the band's tiles are visited, or each packed sequence is addressed
+// through its cu_seqlens offsets with its own lengths.
 //
 // MI355X mapping (32x32x16 MFMAs, fp32 accumulate; P and dS rounded to the
 // input dtype before they enter an MFMA, like P in the forward):
@@ -40,11 +43,11 @@ struct BwdParams {
   const void* v;
   const void* o;
   const void* dout;
-  const float* lse;  // natural-log logsumexp of the forward, contiguous (B, Hq, Nq)
+  const float* lse;  // natural-log logsumexp of the forward, row i of (b, h) at b*lse_sb + h*lse_sh + i
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // workspace, contiguous (B, Hq, Nq)
+  float* delta;  // workspace, laid out like lse
   int64_t q_sb, q_sh, q_sn;  // element strides; the head-dim stride is 1
   int64_t k_sb, k_sh, k_sn;
   int64_t v_sb, v_sh, v_sn;
@@ -62,7 +65,27 @@ struct BwdParams {
   int32_t dkdv_block_slowest, dq_block_slowest;
   // sliding window (the WINDOW instances only): row i sees keys i - win_left .. i + win_right
   int32_t win_left, win_right;
+  // packed variable-length sequences (the VARLEN instances only): sequence b owns tokens
+  // cu_q[b] .. cu_q[b+1]-1 of Q/O/dO/dQ and cu_k[b] .. cu_k[b+1]-1 of K/V/dK/dV; Nq and Nkv hold the
+  // longest lengths, the batch strides are 0
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t total_q, total_k;
+  int64_t lse_sb, lse_sh;  // element offsets of (b, h) in lse and delta; the row index is added
 };
+
+// Lengths and first tokens of sequence b: the dense lengths, or those of the packed sequence read
+// from the offsets, clamped to the token counts so that no offset array can address out of bounds.
+struct SeqSpan {
+  int nq, nkv, q_tok0, k_tok0;
+};
+template <bool VARLEN>
+__device__ __forceinline__ SeqSpan seq_span(const BwdParams& p, int b) {
+  if (!VARLEN) return SeqSpan{p.Nq, p.Nkv, 0, 0};
+  const int cq0 = min(max(p.cu_q[b], 0), p.total_q), cq1 = min(max(p.cu_q[b + 1], cq0), p.total_q);
+  const int ck0 = min(max(p.cu_k[b], 0), p.total_k), ck1 = min(max(p.cu_k[b + 1], ck0), p.total_k);
+  return SeqSpan{min(cq1 - cq0, p.Nq), min(ck1 - ck0, p.Nkv), cq0, ck0};
+}
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -129,7 +152,7 @@ struct BwdCfg {
 // kBwdOnlyV / kBwdOnlyK (two launches, S recomputed in each, to fit wide heads in registers).
 constexpr int kBwdBoth = 0, kBwdOnlyV = 1, kBwdOnlyK = 2;
 
-template <typename T, bool CAUSAL, class Cfg, int PART, bool WINDOW = false>
+template <typename T, bool CAUSAL, class Cfg, int PART, bool WINDOW = false, bool VARLEN = false>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
     fa_bwd_dkdv_kernel(const BwdParams p) {
@@ -174,20 +197,23 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     kvh = (int)(rest % p.Hkv);
     b = (int)(rest / p.Hkv);
   }
+  const SeqSpan sq = seq_span<VARLEN>(p, b);
+  const int nq = sq.nq, nkv = sq.nkv;
+  if (VARLEN && k0 >= nkv) return;  // a key block past this sequence's end (workgroup-uniform)
   const int kw0 = k0 + 32 * wave;  // first key of this wave
   const int my_key = kw0 + (lane & 31);
 
   // K and V rows of the wave's keys as B operands: lane holds row (lane % 32), elements
-  // 16*s + 8*(lane/32) .. +7. Keys past Nkv read as zero.
+  // 16*s + 8*(lane/32) .. +7. Keys past the sequence read as zero.
   vec8 kf[NS], vf[NS];
   {
-    const T* krow = (const T*)p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)my_key * p.k_sn;
-    const T* vrow = (const T*)p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)my_key * p.v_sn;
+    const T* krow = (const T*)p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)(sq.k_tok0 + my_key) * p.k_sn;
+    const T* vrow = (const T*)p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)(sq.k_tok0 + my_key) * p.v_sn;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int col = 16 * s + 8 * (lane >> 5);
-      kf[s] = my_key < p.Nkv ? *(const vec8*)(krow + col) : vec8{};
-      if (DO_K) vf[s] = my_key < p.Nkv ? *(const vec8*)(vrow + col) : vec8{};
+      kf[s] = my_key < nkv ? *(const vec8*)(krow + col) : vec8{};
+      if (DO_K) vf[s] = my_key < nkv ? *(const vec8*)(vrow + col) : vec8{};
     }
   }
   f32x16 dkT[NDB], dvT[NDB];
@@ -198,12 +224,12 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   }
 
   // Work list: (query head of the group, query tile), tiles that can see one of the keys only.
-  const int n_qt = (p.Nq + BQ - 1) / BQ;
+  const int n_qt = (nq + BQ - 1) / BQ;
   int qt0 = CAUSAL ? (k0 / BQ < n_qt ? k0 / BQ : n_qt) : 0, qt_end = n_qt;
   if (WINDOW) {
     // rows that see one of the workgroup's keys: key - win_right <= row <= key + win_left
     const int first = max(0, k0 - p.win_right);
-    const int last = min(p.Nq - 1, k0 + BK - 1 + p.win_left);
+    const int last = min(nq - 1, k0 + BK - 1 + p.win_left);
     qt0 = min(first / BQ, n_qt);
     qt_end = first > last ? qt0 : last / BQ + 1;
   }
@@ -216,13 +242,13 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   auto issue = [&](int w, lds_char_t* qt, lds_char_t* ot, float* ls, float* dl) {
     const int h = kvh * p.group + w / per_head;
     const int q0 = (qt0 + w % per_head) * BQ;
-    const char* qbase = (const char*)p.q + (b * p.q_sb + h * p.q_sh) * 2;
-    const char* obase = (const char*)p.dout + (b * p.do_sb + h * p.do_sh) * 2;
-    dma_tile<D, BQ, NW>(qt, qbase, q_stride, q0, p.Nq, wave_u, q_dma_off);
-    dma_tile<D, BQ, NW>(ot, obase, o_stride, q0, p.Nq, wave_u, o_dma_off);
-    // logsumexp and Delta of the tile's rows: 4 bytes per lane, rows past Nq read as zero
-    const int64_t row0 = ((int64_t)b * p.Hq + h) * p.Nq + q0;
-    const int valid = p.Nq - q0 < BQ ? p.Nq - q0 : BQ;
+    const char* qbase = (const char*)p.q + (b * p.q_sb + h * p.q_sh + (int64_t)sq.q_tok0 * p.q_sn) * 2;
+    const char* obase = (const char*)p.dout + (b * p.do_sb + h * p.do_sh + (int64_t)sq.q_tok0 * p.do_sn) * 2;
+    dma_tile<D, BQ, NW>(qt, qbase, q_stride, q0, nq, wave_u, q_dma_off);
+    dma_tile<D, BQ, NW>(ot, obase, o_stride, q0, nq, wave_u, o_dma_off);
+    // logsumexp and Delta of the tile's rows: 4 bytes per lane, rows past the sequence read as zero
+    const int64_t row0 = b * p.lse_sb + h * p.lse_sh + sq.q_tok0 + q0;
+    const int valid = nq - q0 < BQ ? nq - q0 : BQ;
 #pragma unroll
     for (int part = 0; part < BQ / 64; ++part) {
       if (wave_u == (2 * part) % NW) {
@@ -270,7 +296,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       if (CAUSAL && qrow0 + 31 < kw0) continue;
       // with a window: the block's rows are all outside every key's window
       if (WINDOW && (qrow0 + 31 < kw0 - p.win_right || qrow0 > kw0 + 31 + p.win_left)) continue;
-      if (qrow0 >= p.Nq) continue;
+      if (qrow0 >= nq) continue;
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
       {
         vec8 qa[NS], oa[NS];
@@ -368,9 +394,9 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   if (w < n_work) step(IC<0>(), w);
 
   // ---- epilogue: lane owns key my_key; register r of block db is head-dim 32*db + acc_row(r)
-  if (my_key < p.Nkv) {
-    char* dkrow = (char*)p.dk + (b * p.dk_sb + kvh * p.dk_sh + (int64_t)my_key * p.dk_sn) * 2;
-    char* dvrow = (char*)p.dv + (b * p.dv_sb + kvh * p.dv_sh + (int64_t)my_key * p.dv_sn) * 2;
+  if (my_key < nkv) {
+    char* dkrow = (char*)p.dk + (b * p.dk_sb + kvh * p.dk_sh + (int64_t)(sq.k_tok0 + my_key) * p.dk_sn) * 2;
+    char* dvrow = (char*)p.dv + (b * p.dv_sb + kvh * p.dv_sh + (int64_t)(sq.k_tok0 + my_key) * p.dv_sn) * 2;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -390,7 +416,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
 
 // ------------------------------------------------------------------------------------------------
 // dQ. Grid: ceil(Nq / BW) * Hq * B workgroups (1-D).
-template <typename T, bool CAUSAL, class Cfg, bool WINDOW = false>
+template <typename T, bool CAUSAL, class Cfg, bool WINDOW = false, bool VARLEN = false>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
     fa_bwd_dq_kernel(const BwdParams p) {
@@ -431,16 +457,19 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     h = (int)(rest % p.Hq);
     b = (int)(rest / p.Hq);
   }
+  const SeqSpan sq = seq_span<VARLEN>(p, b);
+  const int nq = sq.nq, nkv = sq.nkv;
+  if (VARLEN && q0 >= nq) return;  // a query block past this sequence's end (workgroup-uniform)
   const int kvh = h / p.group;
   const int wq0 = q0 + 32 * wave;
   const int my_row = wq0 + (lane & 31);
-  const bool row_ok = my_row < p.Nq;
+  const bool row_ok = my_row < nq;
 
-  // Q and dO rows of the wave as B operands (lane holds row lane % 32); rows past Nq are zero.
+  // Q and dO rows of the wave as B operands (lane holds row lane % 32); rows past the sequence are zero.
   vec8 qf[NS], of[NS];
   {
-    const T* qrow = (const T*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)my_row * p.q_sn;
-    const T* orow = (const T*)p.dout + b * p.do_sb + h * p.do_sh + (int64_t)my_row * p.do_sn;
+    const T* qrow = (const T*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)(sq.q_tok0 + my_row) * p.q_sn;
+    const T* orow = (const T*)p.dout + b * p.do_sb + h * p.do_sh + (int64_t)(sq.q_tok0 + my_row) * p.do_sn;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int col = 16 * s + 8 * half;
@@ -448,15 +477,15 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       of[s] = row_ok ? *(const vec8*)(orow + col) : vec8{};
     }
   }
-  const int64_t stat = ((int64_t)b * p.Hq + h) * p.Nq + my_row;
+  const int64_t stat = b * p.lse_sb + h * p.lse_sh + sq.q_tok0 + my_row;
   const float lse2 = row_ok ? p.lse[stat] * kLog2e : 0.f;
   const float dlt = row_ok ? p.delta[stat] : 0.f;
   f32x16 dqT[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqT[db] = f32x16{};
 
-  const char* kbase = (const char*)p.k + (b * p.k_sb + kvh * p.k_sh) * 2;
-  const char* vbase = (const char*)p.v + (b * p.v_sb + kvh * p.v_sh) * 2;
+  const char* kbase = (const char*)p.k + (b * p.k_sb + kvh * p.k_sh + (int64_t)sq.k_tok0 * p.k_sn) * 2;
+  const char* vbase = (const char*)p.v + (b * p.v_sb + kvh * p.v_sh + (int64_t)sq.k_tok0 * p.v_sn) * 2;
   const int k_stride = (int)(p.k_sn * 2), v_stride = (int)(p.v_sn * 2);
   const int k_dma_off = (int)dma_lane_offset<D, true>(lane, k_stride);
   const int v_dma_off = (int)dma_lane_offset<D, false>(lane, v_stride);
@@ -464,11 +493,11 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   int t0 = 0, n_tiles;
   if (WINDOW) {
     const int first = max(0, q0 - p.win_left);
-    const int last = min(p.Nkv - 1, min(q0 + BQ, p.Nq) - 1 + p.win_right);
+    const int last = min(nkv - 1, min(q0 + BQ, nq) - 1 + p.win_right);
     t0 = first / BKV;
     n_tiles = first > last ? 0 : last / BKV + 1 - t0;
   } else {
-    n_tiles = (int)kv_tiles_for_qtile(q0, BQ, p.Nkv, BKV, CAUSAL);
+    n_tiles = (int)kv_tiles_for_qtile(q0, BQ, nkv, BKV, CAUSAL);
   }
   const int wq_last = wq0 + 31;
   const float c = p.c;
@@ -492,8 +521,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     if (j + 1 < n_tiles) {
       lds_char_t* const kn = (lds_char_t*)(S == 0 ? k_st1_raw : k_st0_raw);
       lds_char_t* const vn = (lds_char_t*)(S == 0 ? v_st1_raw : v_st0_raw);
-      dma_tile<D, BKV, NW>(kn, kbase, k_stride, kpos + BKV, p.Nkv, wave_u, k_dma_off);
-      dma_tile<D, BKV, NW>(vn, vbase, v_stride, kpos + BKV, p.Nkv, wave_u, v_dma_off);
+      dma_tile<D, BKV, NW>(kn, kbase, k_stride, kpos + BKV, nkv, wave_u, k_dma_off);
+      dma_tile<D, BKV, NW>(vn, vbase, v_stride, kpos + BKV, nkv, wave_u, v_dma_off);
     }
     if (CAUSAL && kpos > wq_last) return;
     if (WINDOW && (kpos > wq_last + p.win_right || kpos + BKV - 1 < wq0 - p.win_left)) return;
@@ -530,7 +559,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     }
     // register r of block kb: key kpos + 32*kb + acc_row(r, lane) against the lane's row
     const int base = kpos + 4 * half;
-    int limit = p.Nkv - 1 - base;
+    int limit = nkv - 1 - base;
     if (CAUSAL) limit = min(limit, my_row - base);
     if (WINDOW) limit = min(limit, my_row + p.win_right - base);
     const int lower = WINDOW ? my_row - p.win_left - base : -1;  // keys below the window
@@ -578,8 +607,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   };
 
   if (n_tiles > 0) {
-    dma_tile<D, BKV, NW>((lds_char_t*)k_st0_raw, kbase, k_stride, t0 * BKV, p.Nkv, wave_u, k_dma_off);
-    dma_tile<D, BKV, NW>((lds_char_t*)v_st0_raw, vbase, v_stride, t0 * BKV, p.Nkv, wave_u, v_dma_off);
+    dma_tile<D, BKV, NW>((lds_char_t*)k_st0_raw, kbase, k_stride, t0 * BKV, nkv, wave_u, k_dma_off);
+    dma_tile<D, BKV, NW>((lds_char_t*)v_st0_raw, vbase, v_stride, t0 * BKV, nkv, wave_u, v_dma_off);
   }
   int j = 0;
   for (; j + 1 < n_tiles; j += 2) {
@@ -591,7 +620,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   // ---- epilogue: dQ = scale * (dS K), lane owns row my_row; register r of block db is
   // head-dim 32*db + acc_row(r)
   if (row_ok) {
-    char* drow = (char*)p.dq + (b * p.dq_sb + h * p.dq_sh + (int64_t)my_row * p.dq_sn) * 2;
+    char* drow = (char*)p.dq + (b * p.dq_sb + h * p.dq_sh + (int64_t)(sq.q_tok0 + my_row) * p.dq_sn) * 2;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll

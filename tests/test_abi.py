@@ -251,3 +251,37 @@ VL_BAD = [
 @pytest.mark.parametrize("name,over,code", VL_BAD, ids=[b[0] for b in VL_BAD])
 def test_varlen_validation_rejects(name, over, code):
     assert _vl_call(**over) == D_[code]
+
+
+VLB = dict(VL, do=0x70000, dq=0x80000, dk=0x90000, dv=0xA0000, delta=0xB0000, dos=(256, 64, 1), dqs=(256, 64, 1),
+           dks=(128, 64, 1), dvs=(128, 64, 1))
+
+
+def _vlb_call(**over):
+    a = dict(VLB)
+    a.update(over)
+    st3 = lambda s: (ctypes.c_int64 * 3)(*s) if s else None
+    return _lib().fa_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                                a["delta"], a["cq"], a["ck"], a["B"], a["Hq"], a["Hkv"], a["tq"], a["tk"], a["mq"],
+                                a["mk"], a["D"], st3(a["qs"]), st3(a["ks"]), st3(a["vs"]), st3(a["os"]), st3(a["dos"]),
+                                st3(a["dqs"]), st3(a["dks"]), st3(a["dvs"]), a["scale"], a["causal"], a["dtype"], None)
+
+
+VLB_BAD = [
+    ("null_cu", dict(ck=0), "FA_ERR_NULL"), ("null_do", dict(do=0), "FA_ERR_NULL"),
+    ("null_delta", dict(delta=0), "FA_ERR_NULL"), ("null_dq_stride", dict(dqs=None), "FA_ERR_NULL"),
+    ("zero_total", dict(tk=0), "FA_ERR_SHAPE"), ("max_over_total", dict(mq=301), "FA_ERR_SHAPE"),
+    ("zero_batch", dict(B=0), "FA_ERR_SHAPE"), ("misaligned_cu", dict(cq=0x60001), "FA_ERR_LAYOUT"),
+    ("misaligned_dk", dict(dk=0x90004), "FA_ERR_LAYOUT"), ("misaligned_delta", dict(delta=0xB0002), "FA_ERR_LAYOUT"),
+    ("dv_dim_stride", dict(dvs=(128, 64, 2)), "FA_ERR_LAYOUT"), ("dq_zero_token_stride", dict(dqs=(0, 64, 1)),
+                                                                 "FA_ERR_LAYOUT"),
+    ("head_dim", dict(D=24), "FA_ERR_HEAD_DIM"), ("gqa", dict(Hkv=3), "FA_ERR_GQA"),
+    ("dtype", dict(dtype=5), "FA_ERR_DTYPE"), ("scale", dict(scale=float("inf")), "FA_ERR_SCALE"),
+    ("extent_overflow", dict(dos=(256, 1 << 62, 1)), "FA_ERR_SHAPE"),
+    ("row_stride_over_limit", dict(dos=(1 << 55, 64, 1)), "FA_ERR_LAYOUT"),
+]
+
+
+@pytest.mark.parametrize("name,over,code", VLB_BAD, ids=[b[0] for b in VLB_BAD])
+def test_varlen_bwd_validation_rejects(name, over, code):
+    assert _vlb_call(**over) == D_[code]

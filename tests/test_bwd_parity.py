@@ -9,7 +9,7 @@ the forward), reads Delta from the 16-bit O, and rounds each gradient once at th
 those roundings is a relative error of at most half an ulp (2^-9 for bf16, 2^-12 for fp16) on one
 term of a sum of up to N terms, so the error of an element scales with the magnitude of the
 head's gradient, plus the final rounding of the element itself. The bound is therefore
-|gpu - ref| <= A * rms(ref over the head) + R * |ref| with (A, R) = (6e-2, 2e-2) for bf16 and
+|gpu - ref| <= A * rms(ref over the head's rows that receive gradient) + R * |ref| with (A, R) = (6e-2, 2e-2) for bf16 and
 (1e-2, 4e-3) for fp16; the fp16 errors measured on the same shapes are 6-8x below the bf16 ones,
 the ratio of the two ulps, which is what rounding noise (and not a wrong term) looks like.
 """
@@ -44,11 +44,15 @@ def _dout(B, Hq, Nq, D, dtype, seed):
 
 
 def _grad_ratio(got: np.ndarray, ref: np.ndarray, dtype, head_axes=(2, 3), floor: float = 1e-3) -> float:
-    """Worst |got - ref| / (A * rms_head(ref) + R * |ref|) over all elements. A head whose exact
-    gradient vanishes (a single key: dQ = dK = 0) is measured against ``floor``, a small multiple of
-    the dO magnitude the gradients are linear in, instead of its zero rms."""
+    """Worst |got - ref| / (A * rms_head(ref) + R * |ref|) over all elements of (B, H, rows, D) arrays.
+    rms_head is taken over the head's rows that receive any gradient: rows no score reaches (keys
+    past every causal row, rows without keys) are exactly zero and would only dilute the magnitude
+    the roundings scale with. A head whose exact gradient vanishes (a single key: dQ = dK = 0) is
+    measured against ``floor``, a small multiple of the dO magnitude the gradients are linear in."""
     a, r = GRAD_TOL[dtype]
-    rms = np.maximum(np.sqrt(np.mean(ref ** 2, axis=head_axes, keepdims=True)), floor)
+    live = np.any(ref != 0, axis=head_axes[1], keepdims=True)
+    n = np.maximum(np.sum(live, axis=head_axes[0], keepdims=True) * ref.shape[head_axes[1]], 1)
+    rms = np.maximum(np.sqrt(np.sum(ref ** 2, axis=head_axes, keepdims=True) / n), floor)
     bound = a * rms + r * np.abs(ref)
     bound = np.where(bound > 0, bound, 1e-30)
     return float(np.max(np.abs(got - ref) / bound)) if ref.size else 0.0
