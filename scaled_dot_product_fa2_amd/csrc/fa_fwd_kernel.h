@@ -175,6 +175,9 @@ struct IC {
 // reference maximum is raised (and its accumulator rescaled) only when a tile
 // exceeds it by more than this, so probabilities stay below 2^8.
 constexpr float kRescaleHeadroom = 8.0f;
+// Bound on a lane's sum of tile probabilities under which the fast softmax path keeps them without
+// a tile maximum: every probability is then at most 2^14, inside fp16's range (and bf16's).
+constexpr float kFastSumLimit = 16384.0f;
 
 // Fragment read-ahead in the two MFMA loops, in head-dim slices of K (S^T) and in V fragments
 // (P V). Left to itself the compiler issues each LDS read right before the MFMA that consumes it,
@@ -355,13 +358,13 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       if (CAUSAL && kpos > wq_last) return;
       if (WINDOW && (kpos > wq_last + p.win_right || kpos + BKV - 1 < wq_first - p.win_left)) return;
 
-      // ---- S^T = K Q^T
+      // ---- S^T = K Q^T (a lambda: the rare slow softmax path below computes it a second time)
       f32x16 sc[QB][NKB];
+      auto scores = [&]() {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) sc[qb][kb] = f32x16{};
-      {
+          for (int kb = 0; kb < NKB; ++kb) sc[qb][kb] = f32x16{};
         vec8 kf[NS][NKB];
 #pragma unroll
         for (int s = 0; s < NS; ++s)
@@ -383,46 +386,34 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, NKB * QB, 0);
           if (s + LEAD < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NKB, 0);
         }
-      }
+      };
+      scores();
 
       // ---- online softmax in base 2, one query row per lane
-      vec8 pf[QB][NKS];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (mask) {
-          // key = kpos + 4*(lane/32) + koff(kb, r) with koff a compile-time constant; the key is
-          // hidden iff koff > limit, where limit folds the causal bound (key <= row) and the
-          // sequence end (key < Nkv) into one per-lane value.
-          const int qrow = wq_first + qfrag_row(qb, lane);
-          const int base = kpos + 4 * half;
-          int limit = nkv - 1 - base;
-          if (CAUSAL) limit = min(limit, qrow - base);
-          if (WINDOW) limit = min(limit, qrow + p.win_right - base);
-          // with a window, keys below the band are hidden too: koff < lower
-          const int lower = WINDOW ? qrow - p.win_left - base : -1;
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int koff = 32 * kb + 8 * (r >> 2) + (r & 3);
-              const bool hidden = WINDOW ? (koff > limit || koff < lower) : koff > limit;
-              sc[qb][kb][r] = hidden ? -INFINITY : sc[qb][kb][r];
-            }
-        }
-        float mx = -INFINITY;
+      // Scores hidden by the mask become -inf before any maximum or exponential is taken.
+      auto apply_mask = [&](int qb) {
+        // key = kpos + 4*(lane/32) + koff(kb, r) with koff a compile-time constant; the key is
+        // hidden iff koff > limit, where limit folds the causal bound (key <= row) and the
+        // sequence end (key < Nkv) into one per-lane value.
+        const int qrow = wq_first + qfrag_row(qb, lane);
+        const int base = kpos + 4 * half;
+        int limit = nkv - 1 - base;
+        if (CAUSAL) limit = min(limit, qrow - base);
+        if (WINDOW) limit = min(limit, qrow + p.win_right - base);
+        // with a window, keys below the band are hidden too: koff < lower
+        const int lower = WINDOW ? qrow - p.win_left - base : -1;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
-        const float mt = wave_half_max(mx) * c;  // tile maximum of the scaled scores, log2 units
-        const bool grow = mt > m_run[qb] + kRescaleHeadroom;
-        if (__any(grow)) {
-          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.f;
-          m_run[qb] = grow ? mt : m_run[qb];
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int koff = 32 * kb + 8 * (r >> 2) + (r & 3);
+            const bool hidden = WINDOW ? (koff > limit || koff < lower) : koff > limit;
+            sc[qb][kb][r] = hidden ? -INFINITY : sc[qb][kb][r];
+          }
+      };
+      // Probabilities against the current reference maximum m, P = 2^(c*s - m), and their sum over
+      // the lane's keys.
+      auto probabilities = [&](int qb) {
         // a row that has seen no visible key yet keeps -inf; its scores are all -inf here too
         const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
         float rs = 0.f;
@@ -434,6 +425,45 @@ __global__ void __launch_bounds__(Cfg::THREADS)
             sc[qb][kb][r] = pv;
             rs += pv;
           }
+        return rs;
+      };
+      vec8 pf[QB][NKS];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (mask) apply_mask(qb);
+        // Fast path: once a row has a finite reference maximum, the tile's probabilities are taken
+        // against it without computing the tile's maximum first. They are kept when the lane's sum
+        // stays at most kFastSumLimit, which bounds every one of them by it; otherwise (or while a
+        // row has no reference yet, or on a non-finite sum) the tile is scored again and goes
+        // through the maximum below. Either way every probability of the tile is finite and at
+        // most kFastSumLimit, and numerator and denominator share the reference.
+        bool slow = __any(m_run[qb] == -INFINITY);
+        float rs = 0.f;
+        if (!slow) {
+          rs = probabilities(qb);
+          slow = __any(!(rs <= kFastSumLimit));
+          if (slow) {
+            scores();
+            if (mask) apply_mask(qb);
+          }
+        }
+        if (slow) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
+          const float mt = wave_half_max(mx) * c;  // tile maximum of the scaled scores, log2 units
+          const bool grow = mt > m_run[qb] + kRescaleHeadroom;
+          if (__any(grow)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.f;
+            m_run[qb] = grow ? mt : m_run[qb];
+            l_run[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
+          }
+          rs = probabilities(qb);
+        }
         l_run[qb] += rs;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
