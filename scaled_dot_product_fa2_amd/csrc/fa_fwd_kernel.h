@@ -402,30 +402,47 @@ __global__ void __launch_bounds__(Cfg::THREADS)
         if (WINDOW) limit = min(limit, qrow + p.win_right - base);
         // with a window, keys below the band are hidden too: koff < lower
         const int lower = WINDOW ? qrow - p.win_left - base : -1;
+        const int r0 = wq_first + 32 * qb, r1 = r0 + 31;  // rows of this block (wave-uniform)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb) {
+          // Without a window, a 32-key block whose every (row, key) pair is visible needs no
+          // mask and one whose every pair is hidden is cleared whole; only the others are masked
+          // key by key. (The window instances mask every key: their registers are tighter.)
+          if (!WINDOW) {
+            const int k0 = kpos + 32 * kb, k1 = k0 + 31;
+            if (k1 < nkv && (!CAUSAL || k1 <= r0)) continue;
+            if (k0 >= nkv || (CAUSAL && k0 > r1)) {
+              sc[qb][kb] = f32x16{} - INFINITY;
+              continue;
+            }
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int koff = 32 * kb + 8 * (r >> 2) + (r & 3);
             const bool hidden = WINDOW ? (koff > limit || koff < lower) : koff > limit;
             sc[qb][kb][r] = hidden ? -INFINITY : sc[qb][kb][r];
           }
+        }
       };
       // Probabilities against the current reference maximum m, P = 2^(c*s - m), and their sum over
       // the lane's keys.
       auto probabilities = [&](int qb) {
         // a row that has seen no visible key yet keeps -inf; its scores are all -inf here too
         const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-        float rs = 0.f;
+        // four partial sums: four independent add chains instead of one
+        float part[4];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][kb][r], c, -m_use));
             sc[qb][kb][r] = pv;
-            rs += pv;
+            if (kb == 0 && r < 4)
+              part[r] = pv;
+            else
+              part[r & 3] += pv;
           }
-        return rs;
+        return (part[0] + part[1]) + (part[2] + part[3]);
       };
       vec8 pf[QB][NKS];
 #pragma unroll
