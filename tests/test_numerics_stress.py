@@ -7,6 +7,12 @@ the float64 oracles with the same tolerances as the other parity tests.
   nothing, the case where a stale maximum must not lose precision.
 * Very peaked rows: Q scaled by 30, so each row's weight sits on a handful of keys.
 * A single key/value head shared by 32 query heads (MQA) at D = 128.
+* One spiking key: every score near 0 except key 96's, which sits J (log2 units) above the first
+  tile's maximum. The forward's fast softmax path keeps a tile's probabilities without taking its
+  maximum while a lane's sum of them stays at most 2^14. J = 12.5 keeps every row below that
+  bound (a probability of about 2^12.5 kept, inside fp16's range), J = 15.5 puts every row above
+  it (the tile is scored again and the maximum raised), and at J = 13.8 the first tile's noise
+  puts some rows on each side.
 The structured inputs are built in float32 and rounded to the 16-bit dtype once; the oracle sees
 the same rounded tensors. In the monotone cases every key shares a large component, which makes dQ
 a cancelling sum: there dQ is held to the usual tolerance plus the bound on rounding dS to the
@@ -138,3 +144,23 @@ def test_mqa_32_heads(causal):
     for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         ratio = _grad_ratio(pu.to_f64(got), r, torch.bfloat16)
         assert ratio <= 1.0, f"{name}: gradient error ratio {ratio:.3f}"
+
+
+@pytest.mark.parametrize("jump", [6.0, 12.5, 13.8, 15.5, 40.0])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_spiking_key_around_fast_path_bound(jump, D, dtype, causal):
+    print(f"[case] spike J={jump} D={D} {dtype} causal={causal}", flush=True)
+    fa = _fa()
+    N, scale = 200, 1.0 / math.sqrt(D)
+    g = torch.Generator().manual_seed(3400 + int(jump * 10) + D + causal)
+    q = 0.1 * torch.randn(1, 2, N, D, generator=g)
+    q[..., 0] += 1.0 / scale  # scale * q . k along e0 is then k's e0 component
+    k = 0.1 * torch.randn(1, 2, N, D, generator=g)
+    k[:, :, 96, 0] += jump / math.log2(math.e)
+    v = torch.randn(1, 2, N, D, generator=g)
+    qd, kd, vd = (t.to(dtype).to(DEV) for t in (q, k, v))
+    o, lse = fa.fa_fwd(qd, kd, vd, causal=causal)
+    torch.cuda.synchronize()
+    pu.full_check(qd, kd, vd, o, lse, causal, scale, f"spike J={jump} D={D}")
