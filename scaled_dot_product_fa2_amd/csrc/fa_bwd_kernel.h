@@ -563,15 +563,24 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     if (CAUSAL) limit = min(limit, my_row - base);
     if (WINDOW) limit = min(limit, my_row + p.win_right - base);
     const int lower = WINDOW ? my_row - p.win_left - base : -1;  // keys below the window
+    // The per-key test runs only for a tile that crosses the sequence end, the diagonal of the
+    // wave's rows or a window edge (wave-uniform choice between two versions of the loop).
+    auto probs = [&](auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value != 0;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int koff = 32 * kb + 8 * (r >> 2) + (r & 3);
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c, -lse2));
-        pv = (koff > limit || koff < lower) ? 0.f : pv;
-        st[kb][r] = pv * (dpt[kb][r] - dlt);  // dS^T / scale
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int koff = 32 * kb + 8 * (r >> 2) + (r & 3);
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c, -lse2));
+          if (MASKED) pv = (koff > limit || koff < lower) ? 0.f : pv;
+          st[kb][r] = pv * (dpt[kb][r] - dlt);  // dS^T / scale
+        }
+    };
+    if (WINDOW || kpos + BKV > nkv || (CAUSAL && kpos + BKV - 1 > wq0))
+      probs(IC<1>());
+    else
+      probs(IC<0>());
     vec8 sfr[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
