@@ -184,8 +184,9 @@ FA_HD int64_t kv_tiles_for_qtile(int64_t q0, int64_t bq, int64_t nkv, int64_t bk
 // CU when two are resident). Workgroup k takes position pos(k) in the XCD's
 // item list in even rounds and the mirrored position in odd rounds (a snake),
 // where pos() snakes over the CU-major order, so the workgroups that share a
-// CU take mirrored positions. With the causal mask the items are listed
-// longest first, so every CU gets a long query tile paired with a short one.
+// CU take mirrored positions. Items are listed unit by unit; with the causal
+// mask each unit's items are listed longest first, so every CU gets a long
+// query tile paired with a short one while the XCD streams one unit's K/V.
 // The placement only affects balance, never which items are computed.
 constexpr int kCUsPerXCD = 32;
 
@@ -232,9 +233,11 @@ struct Schedule {
       const int units_x = (n_units - x + 7) / 8;
       int64_t m;
       if (causal) {
-        rank = (int)(i / ((int64_t)units_x * group));
-        const int64_t rest = i % ((int64_t)units_x * group);
-        m = rest / group;
+        // unit by unit (the XCD's workgroups stream one unit's K/V together, which its L2 holds),
+        // and within a unit the longest query tiles first, all query heads of the group at each
+        m = i / ((int64_t)group * n_qt);
+        const int64_t rest = i % ((int64_t)group * n_qt);
+        rank = (int)(rest / group);
         g = (int)(rest % group);
       } else {
         m = i / ((int64_t)group * n_qt);

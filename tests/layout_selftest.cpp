@@ -164,11 +164,19 @@ int main() {
               }
               for (long k = 0; k < n_items; ++k) CHECK(seen[k] == 1, "schedule misses or repeats an item");
               for (auto& kv : unit_xcds) CHECK((int)kv.second.size() <= sc.xcd_share(), "unit spread over too many XCDs");
-              // causal: within an XCD the listed items never grow longer
+              // causal: within an XCD, the items of one unit are listed together, longest first
               if (causal)
-                for (int x = 0; x < 8; ++x)
-                  for (long i = 1; i < sc.items_of(x); ++i)
-                    CHECK(sc.item(x, i).qt <= sc.item(x, i - 1).qt, "causal items not longest first");
+                for (int x = 0; x < 8; ++x) {
+                  std::set<int> done;
+                  for (long i = 1; i < sc.items_of(x); ++i) {
+                    const fa::Item a = sc.item(x, i - 1), c = sc.item(x, i);
+                    const int ua = a.b * hkv + a.h / group, uc = c.b * hkv + c.h / group;
+                    if (ua == uc)
+                      CHECK(c.qt <= a.qt, "causal items of a unit not longest first");
+                    else
+                      CHECK(done.insert(ua).second && !done.count(uc), "a unit's items are not listed together");
+                  }
+                }
             }
   // causal balance of the workload of 4 batches x 16 heads x 8 query tiles (2..16 key tiles each)
   // on 2 resident workgroups per CU: every CU gets the same total
