@@ -184,9 +184,12 @@ FA_HD int64_t kv_tiles_for_qtile(int64_t q0, int64_t bq, int64_t nkv, int64_t bk
 // CU when two are resident). Workgroup k takes position pos(k) in the XCD's
 // item list in even rounds and the mirrored position in odd rounds (a snake),
 // where pos() snakes over the CU-major order, so the workgroups that share a
-// CU take mirrored positions. Items are listed unit by unit; with the causal
-// mask each unit's items are listed longest first, so every CU gets a long
-// query tile paired with a short one while the XCD streams one unit's K/V.
+// CU take mirrored positions, so with the causal mask, where items are listed
+// longest first, every CU gets a long query tile paired with a short one.
+// Items are listed unit by unit, longest first within a unit, so that the XCD
+// streams one unit's K/V at a time; when all of an XCD's items run at once
+// (no more items than workgroups) the causal items are instead listed longest
+// first across the XCD's units.
 // The placement only affects balance, never which items are computed.
 constexpr int kCUsPerXCD = 32;
 
@@ -226,13 +229,21 @@ struct Schedule {
     if (g < xcds_used()) g = xcds_used();
     return (int)g;
   }
+  // does XCD x hold no more items than workgroups, so that all of them run at once?
+  FA_HD bool one_round(int x) const { return items_of(x) <= wgs_of(x); }
   // item number i of XCD x (0 <= i < items_of(x))
   FA_HD Item item(int x, int64_t i) const {
     int unit, g, rank;  // rank: position of the query tile in the order items are listed
     if (n_units >= 8) {
       const int units_x = (n_units - x + 7) / 8;
       int64_t m;
-      if (causal) {
+      if (causal && one_round(x)) {
+        // every item of the XCD runs at once: the longest query tiles first across its units
+        rank = (int)(i / ((int64_t)units_x * group));
+        const int64_t rest = i % ((int64_t)units_x * group);
+        m = rest / group;
+        g = (int)(rest % group);
+      } else if (causal) {
         // unit by unit (the XCD's workgroups stream one unit's K/V together, which its L2 holds),
         // and within a unit the longest query tiles first, all query heads of the group at each
         m = i / ((int64_t)group * n_qt);

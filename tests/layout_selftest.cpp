@@ -164,9 +164,15 @@ int main() {
               }
               for (long k = 0; k < n_items; ++k) CHECK(seen[k] == 1, "schedule misses or repeats an item");
               for (auto& kv : unit_xcds) CHECK((int)kv.second.size() <= sc.xcd_share(), "unit spread over too many XCDs");
-              // causal: within an XCD, the items of one unit are listed together, longest first
+              // causal: within an XCD, the items run at once are listed longest first; otherwise the
+              // items of one unit are listed together, longest first
               if (causal)
                 for (int x = 0; x < 8; ++x) {
+                  if (sc.one_round(x)) {
+                    for (long i = 1; i < sc.items_of(x); ++i)
+                      CHECK(sc.item(x, i).qt <= sc.item(x, i - 1).qt, "causal items of one round not longest first");
+                    continue;
+                  }
                   std::set<int> done;
                   for (long i = 1; i < sc.items_of(x); ++i) {
                     const fa::Item a = sc.item(x, i - 1), c = sc.item(x, i);
