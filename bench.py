@@ -20,6 +20,7 @@ Prints ONE JSON line. Extra objects:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                       [--no-backward]
+       python bench.py --sweep | --sweep-backward   (throughput over a fixed list of shapes instead)
 """
 from __future__ import annotations
 
@@ -135,6 +136,57 @@ def backward_timing(w, q, k, v, outs, modes, steps, stream):
     return {"metric": "attention bwd TFLOP/s (five products: 10*B*Hq*Nq*Nkv*D, halved for causal)", "per_mode": res}
 
 
+# Shapes of the throughput sweep (bf16; 65 536 tokens per head for the first two groups).
+SWEEP_FWD = ([(max(1, 65536 // n), 32, 32, n, 64) for n in (512, 1024, 2048, 4096, 8192, 16384)] +
+             [(max(1, 65536 // n), 16, 16, n, 128) for n in (512, 1024, 2048, 4096, 8192, 16384)] +
+             [(1, 32, 8, 16384, 128), (2, 16, 16, 4096, 256), (2, 16, 16, 16384, 256)])
+SWEEP_BWD = [(4, 16, 16, 1024, 128), (4, 16, 16, 4096, 128), (16, 16, 16, 4096, 128), (4, 16, 16, 16384, 128),
+             (1, 32, 8, 16384, 128)]
+
+
+def sweep(backward: bool):
+    """Forward (or backward) TFLOP/s over SWEEP_FWD (SWEEP_BWD), both masks, seeded N(0,1) bf16 inputs:
+    HIP events around back-to-back calls on the launch stream after a warm-up. One JSON line per
+    (shape, mask)."""
+    import torch
+    import scaled_dot_product_fa2_amd as fa
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    for (B, Hq, Hkv, N, D) in (SWEEP_BWD if backward else SWEEP_FWD):
+        g = torch.Generator().manual_seed(7)
+        q = torch.randn(B, Hq, N, D, generator=g).to(torch.bfloat16).to(dev)
+        k = torch.randn(B, Hkv, N, D, generator=g).to(torch.bfloat16).to(dev)
+        v = torch.randn(B, Hkv, N, D, generator=g).to(torch.bfloat16).to(dev)
+        do = torch.randn(B, Hq, N, D, generator=g).to(torch.bfloat16).to(dev) if backward else None
+        o = torch.empty_like(q)
+        lse = torch.empty(B, Hq, N, dtype=torch.float32, device=dev)
+        for causal in (False, True):
+            fwd_flop = 4.0 * B * Hq * N * N * D / (2 if causal else 1)
+            if backward:
+                o, lse = fa.fa_fwd(q, k, v, causal=causal)
+
+                def call():
+                    fa.fa_bwd(q, k, v, o, lse, do, causal=causal, stream=st)
+                work, reps = 2.5 * fwd_flop, 5
+            else:
+                call = fa.fa_fwd_call(q, k, v, o, lse, causal=causal, stream=st)
+                work, reps = fwd_flop, max(5, min(200, int(1e14 / fwd_flop)))
+            for _ in range(max(3, reps // 2)):
+                call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(st)
+            for _ in range(reps):
+                call()
+            e1.record(st)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            print(json.dumps({"pass": "backward" if backward else "forward", "B": B, "Hq": Hq, "Hkv": Hkv, "N": N,
+                              "D": D, "causal": causal, "ms": round(ms, 4),
+                              "tflops": round(work / (ms / 1e3) / 1e12, 1)}), flush=True)
+        del q, k, v, do, o, lse
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +195,9 @@ def main():
     ap.add_argument("--workload", default="b4h16n1024d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark: forward TFLOP/s over a fixed list of shapes, one JSON line each")
+    ap.add_argument("--sweep-backward", action="store_true", help="the same for the backward (five-product TFLOP/s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB, 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -154,6 +209,10 @@ def main():
     import torch
     import workloads
     import scaled_dot_product_fa2_amd as fa
+
+    if args.sweep or args.sweep_backward:
+        sweep(backward=args.sweep_backward)
+        return
 
     if args.copy_calibration:
         n = 256 * 1024 * 1024 // 4
