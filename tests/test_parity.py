@@ -148,3 +148,20 @@ def test_workload_sampled(name):
         rows = pu.sample_rows(w.Nq, 128, rng)
         r, e = pu.sampled_check(q, k, v, o, lse, causal, w.scale, _heads(w, rng, 6), rows, name)
         print(f"[result] {name} causal={causal} worst O ratio {r:.3f} worst LSE err {e:.2e}", flush=True)
+
+
+# More items than resident workgroups under the causal mask: each XCD lists its items unit by unit
+# (longest first within a unit) and every workgroup runs several of them.
+MANY_ITEMS = [(16, 16, 16, 520, 128, torch.bfloat16), (8, 16, 4, 1000, 64, torch.float16)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,D,dtype", MANY_ITEMS,
+                         ids=[f"b{b}h{hq}kv{hkv}n{n}d{d}" for b, hq, hkv, n, d, _ in MANY_ITEMS])
+def test_causal_many_items_per_workgroup(B, Hq, Hkv, N, D, dtype):
+    _announce(f"causal, many items per workgroup: B={B} Hq={Hq} Hkv={Hkv} N={N} D={D} {dtype}")
+    fa = _fa()
+    plan = fa.fa_fwd_plan(B, Hq, Hkv, N, N, D, True, 1 if dtype == torch.bfloat16 else 0)
+    assert B * Hq * ((N + plan["block_q"] - 1) // plan["block_q"]) > plan["grid"]
+    q, k, v = workloads.make_random(B, Hq, Hkv, N, N, D, dtype, seed=5100 + D)
+    q, k, v, o, lse = _run(q, k, v, True)
+    pu.full_check(q, k, v, o, lse, True, 1.0 / math.sqrt(D), f"many items b{B} h{Hq}/{Hkv} n{N} d{D}")
