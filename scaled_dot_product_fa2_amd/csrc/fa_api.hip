@@ -1,6 +1,7 @@
 // fa_api.hip - C ABI of the gfx950 attention forward and backward: validation,
-// launch plan, dispatch over (dtype, head_dim, causal) instances. The
-// declarations and the contract of every entry point are in include/fa.h.
+// launch plan, dispatch over (dtype, head_dim, mask) instances (defined in
+// fa_fwd_inst.hip and fa_bwd_inst.hip). The declarations and the contract of
+// every entry point are in include/fa.h.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -8,26 +9,14 @@
 #include <limits>
 
 #include "fa.h"
-#include "fa_bwd_kernel.h"
-#include "fa_fwd_kernel.h"
+#include "fa_launch.h"
 #include "fa_layout.h"
 
 namespace {
 
+using fa::CfgFor;
 using fa::FwdParams;
-using fa::TileCfg;
-
-// Tile configuration per head dim: four waves per workgroup, one 32-row query block per wave,
-// and as many waves per SIMD as the registers allow (occupancy is what hides the softmax behind
-// the other waves' MFMAs). D <= 32: four waves per SIMD; D = 64: three; D = 128: two (64 KiB of
-// LDS per workgroup, two per CU); D = 256: two, with 32-key tiles (64 KiB of LDS per workgroup).
-template <int D>
-struct CfgFor;
-template <> struct CfgFor<16> { typedef TileCfg<16, 4, 1, 64, 4> type; };
-template <> struct CfgFor<32> { typedef TileCfg<32, 4, 1, 64, 4> type; };
-template <> struct CfgFor<64> { typedef TileCfg<64, 4, 1, 64, 3> type; };
-template <> struct CfgFor<128> { typedef TileCfg<128, 4, 1, 64, 2> type; };
-template <> struct CfgFor<256> { typedef TileCfg<256, 4, 1, 32, 2> type; };
+using fa::kNumCUs;
 
 struct PlanInfo {
   int threads, bq, bkv, lds, wgs_per_cu;
@@ -38,8 +27,6 @@ PlanInfo plan_info() {
   typedef typename CfgFor<D>::type C;
   return PlanInfo{C::THREADS, C::BQ, C::BKV, C::LDS_BYTES, C::WAVES_PER_SIMD * 4 / C::NW};
 }
-
-constexpr int kNumCUs = 256;  // MI355X
 
 bool plan_for_d(int64_t D, PlanInfo* out) {
   switch (D) {
@@ -106,22 +93,14 @@ int check_strides(const int64_t* st, bool is_output, int64_t B, int64_t H, int64
   return FA_OK;
 }
 
-template <typename T, bool CAUSAL, int D, bool WINDOW = false, bool VARLEN = false>
-int launch(const FwdParams& p, int64_t grid, hipStream_t stream) {
-  typedef typename CfgFor<D>::type C;
-  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, CAUSAL, C, WINDOW, VARLEN>), dim3((unsigned)grid), dim3(C::THREADS), 0,
-                     stream, p);
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
-}
-
 template <typename T, bool CAUSAL, bool WINDOW = false, bool VARLEN = false>
 int launch_d(int64_t D, const FwdParams& p, int64_t grid, hipStream_t stream) {
   switch (D) {
-    case 16: return launch<T, CAUSAL, 16, WINDOW, VARLEN>(p, grid, stream);
-    case 32: return launch<T, CAUSAL, 32, WINDOW, VARLEN>(p, grid, stream);
-    case 64: return launch<T, CAUSAL, 64, WINDOW, VARLEN>(p, grid, stream);
-    case 128: return launch<T, CAUSAL, 128, WINDOW, VARLEN>(p, grid, stream);
-    case 256: return launch<T, CAUSAL, 256, WINDOW, VARLEN>(p, grid, stream);
+    case 16: return fa::launch_fwd<T, CAUSAL, 16, WINDOW, VARLEN>(p, grid, stream);
+    case 32: return fa::launch_fwd<T, CAUSAL, 32, WINDOW, VARLEN>(p, grid, stream);
+    case 64: return fa::launch_fwd<T, CAUSAL, 64, WINDOW, VARLEN>(p, grid, stream);
+    case 128: return fa::launch_fwd<T, CAUSAL, 128, WINDOW, VARLEN>(p, grid, stream);
+    case 256: return fa::launch_fwd<T, CAUSAL, 256, WINDOW, VARLEN>(p, grid, stream);
     default: return FA_ERR_HEAD_DIM;
   }
 }
@@ -175,77 +154,14 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   return FA_OK;
 }
 
-// ---- backward: per head dim, the dK/dV kernel (32 keys per wave, 64-row query tiles) and the
-// dQ kernel (32 query rows per wave, 64-key tiles; 32 at D = 256). SPLIT_KV runs dV and dK as two
-// launches (S recomputed in each) so the registers of a wave hold one accumulator set, not two.
-// Waves per SIMD: dK/dV two up to D = 64, dQ two up to D = 128, otherwise one (register limits).
-#ifndef BWD_SPLIT_MIN_D
-#define BWD_SPLIT_MIN_D 256
-#endif
-#ifndef BWD_DQ_W2_MAX_D
-#define BWD_DQ_W2_MAX_D 128
-#endif
-template <int D>
-struct BwdCfgFor {
-  static constexpr bool SPLIT_KV = D >= BWD_SPLIT_MIN_D;
-  static constexpr int W_KV = D <= 64 ? 2 : (SPLIT_KV && D <= 128 ? 2 : 1);
-  static constexpr int W_Q = D <= BWD_DQ_W2_MAX_D ? 2 : 1;
-  typedef fa::BwdCfg<D, 4, 64, W_KV> dkdv;
-  typedef fa::BwdCfg<D, 4, D >= 256 ? 32 : 64, W_Q> dq;
-};
-
-
-template <typename T, bool CAUSAL, int D, bool WINDOW = false, bool VARLEN = false>
-int launch_bwd(fa::BwdParams p, hipStream_t stream) {
-  typedef typename BwdCfgFor<D>::dkdv CK;
-  typedef typename BwdCfgFor<D>::dq CQ;
-  // row block slowest under the causal mask (longest first), and when a grid is at most about two
-  // rounds of resident workgroups (the blocks of a head then run together on one XCD and share its
-  // streamed tiles in L2); otherwise the blocks of a head are dispatched consecutively
-  const int64_t kv_wgs = (int64_t)((p.Nkv + CK::BW - 1) / CK::BW) * p.Hkv * p.B;
-  const int64_t q_wgs = (int64_t)((p.Nq + CQ::BW - 1) / CQ::BW) * p.Hq * p.B;
-  p.dkdv_block_slowest = CAUSAL || kv_wgs <= 2 * kNumCUs * (CK::WAVES_PER_SIMD * 4 / CK::NW);
-  p.dq_block_slowest = CAUSAL || q_wgs <= 2 * kNumCUs * (CQ::WAVES_PER_SIMD * 4 / CQ::NW);
-  constexpr int RPB = 256 / (D / 8);
-  // Delta is per token: packed sequences run it as one batch of total_q rows, which is the
-  // (Hq, total_q) layout of their logsumexp
-  fa::BwdParams pd = p;
-  if (VARLEN) {
-    pd.B = 1;
-    pd.Nq = p.total_q;
-    pd.o_sb = 0;
-    pd.do_sb = 0;
-  }
-  const int64_t rows = (int64_t)pd.B * pd.Hq * pd.Nq;
-  hipLaunchKernelGGL((fa::fa_bwd_delta_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, pd);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  const dim3 kv_grid((unsigned)((int64_t)((p.Nkv + CK::BW - 1) / CK::BW) * p.Hkv * p.B));
-  if constexpr (BwdCfgFor<D>::SPLIT_KV) {
-    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyV, WINDOW, VARLEN>), kv_grid,
-                       dim3(CK::THREADS), 0, stream, p);
-    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdOnlyK, WINDOW, VARLEN>), kv_grid,
-                       dim3(CK::THREADS), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<T, CAUSAL, CK, fa::kBwdBoth, WINDOW, VARLEN>), kv_grid,
-                       dim3(CK::THREADS), 0, stream, p);
-  }
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<T, CAUSAL, CQ, WINDOW, VARLEN>),
-                     dim3((unsigned)((int64_t)((p.Nq + CQ::BW - 1) / CQ::BW) * p.Hq * p.B)),
-                     dim3(CQ::THREADS), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
-}
-
 template <typename T, bool CAUSAL, bool WINDOW = false, bool VARLEN = false>
 int launch_bwd_d(int64_t D, const fa::BwdParams& p, hipStream_t stream) {
   switch (D) {
-    case 16: return launch_bwd<T, CAUSAL, 16, WINDOW, VARLEN>(p, stream);
-    case 32: return launch_bwd<T, CAUSAL, 32, WINDOW, VARLEN>(p, stream);
-    case 64: return launch_bwd<T, CAUSAL, 64, WINDOW, VARLEN>(p, stream);
-    case 128: return launch_bwd<T, CAUSAL, 128, WINDOW, VARLEN>(p, stream);
-    case 256: return launch_bwd<T, CAUSAL, 256, WINDOW, VARLEN>(p, stream);
+    case 16: return fa::launch_bwd<T, CAUSAL, 16, WINDOW, VARLEN>(p, stream);
+    case 32: return fa::launch_bwd<T, CAUSAL, 32, WINDOW, VARLEN>(p, stream);
+    case 64: return fa::launch_bwd<T, CAUSAL, 64, WINDOW, VARLEN>(p, stream);
+    case 128: return fa::launch_bwd<T, CAUSAL, 128, WINDOW, VARLEN>(p, stream);
+    case 256: return fa::launch_bwd<T, CAUSAL, 256, WINDOW, VARLEN>(p, stream);
     default: return FA_ERR_HEAD_DIM;
   }
 }

@@ -90,15 +90,10 @@ __device__ __forceinline__ SeqSpan seq_span(const BwdParams& p, int b) {
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // Fragment read-ahead of the gradient kernels, in fragments (as in the forward's loops).
-#ifndef BWD_LEAD
-#define BWD_LEAD 3
-#endif
-constexpr int kBwdLead = BWD_LEAD;
+constexpr int kBwdLead = 3;
 // The dQ kernel's score loop at D >= 128 under a mask holds the mask's row bounds as well; one
 // fragment less read-ahead there keeps it inside the register file.
-#ifndef BWD_DQ_MASKED_LEAD
-#define BWD_DQ_MASKED_LEAD 2
-#endif
+constexpr int kBwdDqMaskedLead = 2;
 
 // Compile-time part of the row-fragment read of rows 32*qb + (lane % 32), chunk 2*s + lane/32, of a
 // tile in the transposing (unswizzled) layout; the per-lane part depends on s only through its parity.
@@ -548,7 +543,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           st[kb] = Elem<T>::mfma(ka[s][kb], qf[s], st[kb]);
           dpt[kb] = Elem<T>::mfma(va[s][kb], of[s], dpt[kb]);
         }
-      constexpr int LEAD_S = D >= 128 && (CAUSAL || WINDOW) ? BWD_DQ_MASKED_LEAD : kBwdLead;
+      constexpr int LEAD_S = D >= 128 && (CAUSAL || WINDOW) ? kBwdDqMaskedLead : kBwdLead;
       constexpr int LEAD = LEAD_S < NS ? LEAD_S : NS;
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * NKB * LEAD, 0);
 #pragma unroll
