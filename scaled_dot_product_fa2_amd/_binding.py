@@ -102,6 +102,23 @@ def _strides(t: torch.Tensor):
     return (ctypes.c_int64 * 4)(*t.stride())
 
 
+def _on_device(dev: torch.device, **tensors) -> None:
+    """Every tensor must be a GPU tensor on `dev`: the C ABI takes raw pointers and cannot tell a host
+    pointer, or one on another GPU, from a valid device pointer."""
+    for name, t in tensors.items():
+        if not t.is_cuda or t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev} (all tensors on one GPU)")
+
+
+def _stream_for(dev: torch.device, stream):
+    """The stream to launch on (default: the current stream of `dev`); it must belong to `dev`."""
+    if stream is None:
+        return torch.cuda.current_stream(dev)
+    if stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, expected {dev}")
+    return stream
+
+
 class FaCall:
     """A validated, pre-marshalled fa_fwd call on fixed tensors: calling it enqueues one forward.
 
@@ -129,8 +146,7 @@ def fa_fwd_call(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
     _, Hkv, Nkv, _ = k.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    stream = _stream_for(q.device, stream)
     strides = [_strides(t) for t in (q, k, v, out)]
     args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
             ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
@@ -152,8 +168,9 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = 
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, H, N, D)")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if not q.is_cuda:
         raise ValueError("q, k, v must be GPU tensors")
+    _on_device(q.device, k=k, v=v)
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
         raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
     B, Hq, Nq, D = q.shape
@@ -164,14 +181,14 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = 
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, Hq, Nq, D), dtype=q.dtype, device=q.device)
-    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
-        raise ValueError("out must match q in shape, dtype and device")
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     elif lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (B, Hq, Nq) tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    _on_device(q.device, out=out, lse=lse)
+    stream = _stream_for(q.device, stream)
     code = load_library().fa_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
         B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(out),
@@ -192,8 +209,9 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
     not passed. Same dtype, stride and alignment rules as ``fa_fwd``. ``window=(left, right)``
     runs the backward of ``fa_fwd_window`` (then ``causal`` must be False).
     """
-    if not all(t.is_cuda for t in (q, k, v, o, lse, dout)):
+    if not q.is_cuda:
         raise ValueError("all tensors must be on the GPU")
+    _on_device(q.device, k=k, v=v, o=o, lse=lse, dout=dout)
     if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype) or q.dtype not in _DTYPES:
         raise ValueError("q, k, v, o, dout must share one dtype, float16 or bfloat16")
     B, Hq, Nq, D = q.shape
@@ -208,14 +226,14 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
-            raise ValueError(f"{name} must match the shape, dtype and device of its input")
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{name} must match the shape and dtype of its input")
     if delta is None:
         delta = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     elif delta.shape != (B, Hq, Nq) or delta.dtype != torch.float32 or not delta.is_contiguous():
         raise ValueError("delta must be a contiguous float32 (B, Hq, Nq) tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    _on_device(q.device, dq=dq, dk=dk, dv=dv, delta=delta)
+    stream = _stream_for(q.device, stream)
     common = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
               B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(o), _strides(dout),
@@ -238,8 +256,9 @@ def fa_fwd_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, window_l
     """Attention forward with a sliding window: query row i sees keys i - window_left .. i + window_right
     (-1 = unbounded on that side). Same tensors, rules and return values as ``fa_fwd``; a row whose
     window holds no key gets O = 0 and LSE = -inf."""
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if not q.is_cuda:
         raise ValueError("q, k, v must be GPU tensors")
+    _on_device(q.device, k=k, v=v)
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
         raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
     B, Hq, Nq, D = q.shape
@@ -250,14 +269,14 @@ def fa_fwd_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, window_l
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, Hq, Nq, D), dtype=q.dtype, device=q.device)
-    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
-        raise ValueError("out must match q in shape, dtype and device")
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     elif lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (B, Hq, Nq) tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    _on_device(q.device, out=out, lse=lse)
+    stream = _stream_for(q.device, stream)
     code = load_library().fa_fwd_window(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
         B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(out),
@@ -276,8 +295,9 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
     q: (total_q, Hq, D), k, v: (total_k, Hkv, D) token-major GPU tensors; cu_seqlens_q/k: int32 GPU
     tensors of B + 1 offsets. Returns o (total_q, Hq, D) and lse (Hq, total_q) float32.
     """
-    if not all(t.is_cuda for t in (q, k, v, cu_seqlens_q, cu_seqlens_k)):
+    if not q.is_cuda:
         raise ValueError("all tensors must be on the GPU")
+    _on_device(q.device, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k)
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
         raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
@@ -293,14 +313,14 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
-        raise ValueError("out must match q in shape, dtype and device")
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
     if lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
     elif lse.shape != (Hq, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (Hq, total_q) tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    _on_device(q.device, out=out, lse=lse)
+    stream = _stream_for(q.device, stream)
 
     def st3(t):
         return (ctypes.c_int64 * 3)(*t.stride())
@@ -325,8 +345,9 @@ def fa_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     o and lse are that call's outputs ((total_q, Hq, D) and (Hq, total_q) float32), dout the gradient
     of the loss with respect to o. The float32 workspace ``delta`` is (Hq, total_q).
     """
-    if not all(t.is_cuda for t in (q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k)):
+    if not q.is_cuda:
         raise ValueError("all tensors must be on the GPU")
+    _on_device(q.device, k=k, v=v, o=o, lse=lse, dout=dout, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k)
     if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype) or q.dtype not in _DTYPES:
         raise ValueError("q, k, v, o, dout must share one dtype, float16 or bfloat16")
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
@@ -346,14 +367,14 @@ def fa_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
-            raise ValueError(f"{name} must match the shape, dtype and device of its input")
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{name} must match the shape and dtype of its input")
     if delta is None:
         delta = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
     elif delta.shape != (Hq, total_q) or delta.dtype != torch.float32 or not delta.is_contiguous():
         raise ValueError("delta must be a contiguous float32 (Hq, total_q) tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    _on_device(q.device, dq=dq, dk=dk, dv=dv, delta=delta)
+    stream = _stream_for(q.device, stream)
 
     def st3(t):
         return (ctypes.c_int64 * 3)(*t.stride())
