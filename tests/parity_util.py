@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import math
+import os
 from typing import Dict, Iterable, List, Sequence, Tuple
 
 import numpy as np
@@ -73,6 +74,26 @@ def sampled_check(q, k, v, o, lse, causal, scale, heads: Iterable[Tuple[int, int
             vc[b:b + 1, kvh:kvh + 1].to(torch.float64).numpy(), 0, 0, rows, causal=causal,
             scale=f32_scale(scale))
         r, e = assert_close(o_cpu[b, h, rows].to(torch.float64).numpy(), l_cpu[b, h, rows].to(torch.float64).numpy(),
+                            o_ref, l_ref, q.dtype, f"{what} b={b} h={h}")
+        worst_r, worst_e = max(worst_r, r), max(worst_e, e)
+    return worst_r, worst_e
+
+
+def pool_workers() -> int:
+    """Host processes for the pooled oracle: the cores this process may use, at most 15 (the GPU
+    process itself is the sixteenth)."""
+    return max(1, min(15, len(os.sched_getaffinity(0))))
+
+
+def full_check_pool(q, k, v, o, lse, causal, scale, what=""):
+    """Compare every output element with the oracle, computed one (batch, head) per task in a pool of
+    host processes. Returns the worst O error ratio and the worst LSE error over all elements."""
+    qn, kn, vn = (t.detach().cpu().float().numpy() for t in (q, k, v))  # exact upcast of 16-bit values
+    res, _ = oracle.attention_ref_pool(qn, kn, vn, causal=causal, scale=f32_scale(scale), workers=pool_workers())
+    o_cpu, l_cpu = o.detach().cpu(), lse.detach().cpu()
+    worst_r, worst_e = 0.0, 0.0
+    for (b, h), (o_ref, l_ref) in sorted(res.items()):
+        r, e = assert_close(o_cpu[b, h].to(torch.float64).numpy(), l_cpu[b, h].to(torch.float64).numpy(),
                             o_ref, l_ref, q.dtype, f"{what} b={b} h={h}")
         worst_r, worst_e = max(worst_r, r), max(worst_e, e)
     return worst_r, worst_e

@@ -1,8 +1,8 @@
 """GPU parity of the HIP attention forward against the float64 oracle.
 
-Small shapes are compared element by element; the five named workloads are
-compared in full where the oracle finishes in seconds and on sampled rows
-otherwise. Every case prints its name before it runs.
+Every case compares every output element with the oracle, the five named
+workloads included (the three large ones through the pooled oracle on the host
+cores). Every case prints its name before it runs.
 """
 import math
 
@@ -122,13 +122,17 @@ def _workload_case(name, causal):
 def test_workload_tiny_full():
     for causal in (False, True):
         w, q, k, v, o, lse = _workload_case("tiny", causal)
-        pu.full_check(q, k, v, o, lse, causal, w.scale, f"tiny causal={causal}")
+        r, e = pu.full_check(q, k, v, o, lse, causal, w.scale, f"tiny causal={causal}")
+        print(f"[result] tiny causal={causal}: every element, worst O error ratio {r:.3f}, worst LSE error {e:.2e}",
+              flush=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_workload_b4h16n1024d128_full(causal):
     w, q, k, v, o, lse = _workload_case("b4h16n1024d128", causal)
-    pu.full_check(q, k, v, o, lse, causal, w.scale, f"b4h16n1024d128 causal={causal}")
+    r, e = pu.full_check(q, k, v, o, lse, causal, w.scale, f"b4h16n1024d128 causal={causal}")
+    print(f"[result] b4h16n1024d128 causal={causal}: every element, worst O error ratio {r:.3f}, "
+          f"worst LSE error {e:.2e}", flush=True)
 
 
 def _heads(w, rng, n):
@@ -139,15 +143,20 @@ def _heads(w, rng, n):
 
 
 @pytest.mark.parametrize("name", ["z128h8n1024d64_strided", "b2h16n4096d256_peaked", "gqa_b1h32kv8n16384d128"])
-def test_workload_sampled(name):
+def test_workload_full(name):
+    """Every O and LSE element of the three large workloads against the float64 oracle, which runs one
+    (batch, head) per task on the host cores. Sampled rows (first, last, tile edges, random) of six heads
+    are compared first as a quick pre-check."""
     w = workloads.WORKLOADS[name]
     for causal in w.causal_modes:
         w, q, k, v, o, lse = _workload_case(name, causal)
         assert torch.isfinite(o).all() and torch.isfinite(lse).all()
         rng = np.random.default_rng(w.seed)
         rows = pu.sample_rows(w.Nq, 128, rng)
-        r, e = pu.sampled_check(q, k, v, o, lse, causal, w.scale, _heads(w, rng, 6), rows, name)
-        print(f"[result] {name} causal={causal} worst O ratio {r:.3f} worst LSE err {e:.2e}", flush=True)
+        pu.sampled_check(q, k, v, o, lse, causal, w.scale, _heads(w, rng, 6), rows, name)
+        r, e = pu.full_check_pool(q, k, v, o, lse, causal, w.scale, name)
+        print(f"[result] {name} causal={causal}: every element, worst O error ratio {r:.3f}, "
+              f"worst LSE error {e:.2e}", flush=True)
 
 
 # More items than resident workgroups under the causal mask: each XCD lists its items unit by unit
