@@ -175,22 +175,41 @@ FA_HD int64_t kv_tiles_for_qtile(int64_t q0, int64_t bq, int64_t nkv, int64_t bk
 // ---------------------------------------------------------------------------
 // Work schedule. An item is one (batch, query head, query tile). A "unit" is
 // one (batch, key/value head) pair with its `group` query heads; all items of
-// a unit read the same K/V, so they are kept on one XCD (workgroup ids are
-// dealt round-robin to the 8 XCDs, each with its own L2). With fewer than 8
-// units, each unit's items are spread over 8 / n_units XCDs.
+// a unit read the same K/V. Workgroup ids are dealt round-robin to the 8 XCDs,
+// each with its own L2, so the XCD that runs an item decides which L2 its K/V
+// stream goes through.
+//
+// Placement. The first 8*W units (W = n_units / 8) are whole units: unit
+// x + 8m belongs to XCD x, which keeps its K/V in one L2. The R = n_units % 8
+// leftover units are dealt so that every XCD holds the same work to within one
+// item:
+//  * R = 1, 2 or 4: leftover unit r takes its own share of s = 8 / R XCDs,
+//    its items (longest query tile first under the causal mask) dealt over
+//    them in a snake (still one unit per L2);
+//  * R = 3, 5, 6 or 7: over all eight XCDs. Under the causal mask the leftover
+//    items are listed longest query tile first (then unit, then head) and
+//    dealt over the XCDs in a snake; without it they are listed unit by unit
+//    and XCD x takes a contiguous run of (L - x + 7) / 8 of the L items.
+//
+// Order of an XCD's list:
+//  * causal, all of the XCD's items running at once (no more items than
+//    workgroups): longest query tile first over all of them;
+//  * causal, several rounds: the leftover items first (longest first), then
+//    the whole units one at a time (the XCD's workgroups stream one unit's K/V
+//    together, which its L2 holds), longest first within a unit and all query
+//    heads of the group at each query tile;
+//  * without the mask: the whole units unit by unit (head, then query tile),
+//    then the leftover items.
 //
 // The grid holds at most a few workgroups per CU. The dispatcher deals an
 // XCD's workgroups k = 0, 1, ... over its 32 CUs first (k and k + 32 share a
 // CU when two are resident). Workgroup k takes position pos(k) in the XCD's
 // item list in even rounds and the mirrored position in odd rounds (a snake),
 // where pos() snakes over the CU-major order, so the workgroups that share a
-// CU take mirrored positions, so with the causal mask, where items are listed
+// CU take mirrored positions: with the causal mask, where items are listed
 // longest first, every CU gets a long query tile paired with a short one.
-// Items are listed unit by unit, longest first within a unit, so that the XCD
-// streams one unit's K/V at a time; when all of an XCD's items run at once
-// (no more items than workgroups) the causal items are instead listed longest
-// first across the XCD's units.
-// The placement only affects balance, never which items are computed.
+// The placement only affects balance and cache reuse, never which items are
+// computed.
 constexpr int kCUsPerXCD = 32;
 
 struct Item {
@@ -205,75 +224,127 @@ struct Schedule {
   bool causal;
   int grid;     // workgroups launched
 
-  FA_HD int xcd_share() const { return n_units >= 8 ? 1 : 8 / n_units; }
-  // XCDs that receive items
-  FA_HD int xcds_used() const { return n_units >= 8 ? 8 : n_units * xcd_share(); }
-  // number of items of XCD x
-  FA_HD int64_t items_of(int x) const {
-    if (x >= xcds_used()) return 0;
-    const int64_t per_unit = (int64_t)group * n_qt;
-    if (n_units >= 8) {
-      const int64_t units_x = (n_units - x + 7) / 8;
-      return units_x * per_unit;
+  FA_HD int whole() const { return n_units / 8; }  // whole units per XCD
+  FA_HD int rest() const { return n_units % 8; }   // leftover units
+  FA_HD int64_t per_unit() const { return (int64_t)group * n_qt; }
+  FA_HD int64_t n_items() const { return (int64_t)n_units * per_unit(); }
+  FA_HD int64_t n_whole_of() const { return (int64_t)whole() * per_unit(); }  // whole-unit items per XCD
+  // leftover units with their own XCD share (R divides 8), and the share
+  FA_HD bool shared_rest() const { return rest() == 1 || rest() == 2 || rest() == 4; }
+  FA_HD int share() const { return rest() > 0 ? 8 / rest() : 8; }
+
+  // The leftover entries of XCD x are taken from a leftover list (one unit's items when the
+  // leftover units have their own shares, else all leftover items) in a snake over its m XCDs:
+  // sweep k of m consecutive entries goes to XCDs 0 .. m-1 for even k and m-1 .. 0 for odd k, so no
+  // XCD always receives the longer item of a sweep. The entries of XCD-in-share a are therefore
+  // 2m*k + a and 2m*k + 2m-1-a (k = 0, 1, ...). m is 8 / R (shared) or 8, a power of two.
+  FA_HD int lo_shift() const { return !shared_rest() ? 3 : rest() == 1 ? 3 : rest() == 2 ? 2 : 1; }
+  FA_HD int lo_a(int x) const { return shared_rest() ? x % share() : x; }
+  FA_HD int64_t lo_len() const { return shared_rest() ? per_unit() : (int64_t)rest() * per_unit(); }
+  // entries e < n of XCD x's sequence
+  FA_HD int64_t lo_count_below(int x, int64_t n) const {
+    const int a = lo_a(x), period = 2 << lo_shift();
+    const int64_t q = n >> (lo_shift() + 1);
+    const int r = (int)(n & (period - 1));
+    return 2 * q + (r > a ? 1 : 0) + (r > period - 1 - a ? 1 : 0);
+  }
+  // entry number k of XCD x's sequence
+  FA_HD int64_t lo_entry(int x, int64_t k) const {
+    const int a = lo_a(x), period = 2 << lo_shift();
+    return (k >> 1) * period + ((k & 1) ? period - 1 - a : a);
+  }
+  // leftover items of XCD x
+  FA_HD int64_t left_of(int x) const {
+    if (rest() == 0) return 0;
+    if (!causal && !shared_rest()) {  // a contiguous run
+      const int64_t L = lo_len();
+      return L > x ? (L - x + 7) / 8 : 0;
     }
-    const int s = xcd_share(), sub = x % s;
-    return (per_unit - sub + s - 1) / s;
+    return lo_count_below(x, lo_len());
+  }
+  // number of items of XCD x
+  FA_HD int64_t items_of(int x) const { return n_whole_of() + left_of(x); }
+  // one more than the highest XCD that receives items (the grid must reach it)
+  FA_HD int xcds_used() const {
+    for (int x = 7; x > 0; --x)
+      if (items_of(x) > 0) return x + 1;
+    return 1;
   }
   // workgroups of XCD x
   FA_HD int wgs_of(int x) const { return x < grid ? (grid - x + 7) / 8 : 0; }
   // grid for at most `max_grid` workgroups: no more than there are items, but at least one
   // workgroup on every XCD that has items
   FA_HD int choose_grid(int64_t max_grid) const {
-    const int64_t n_items = (int64_t)n_units * group * n_qt;
-    int64_t g = max_grid < n_items ? max_grid : n_items;
+    int64_t g = max_grid < n_items() ? max_grid : n_items();
     if (g < xcds_used()) g = xcds_used();
     return (int)g;
   }
   // does XCD x hold no more items than workgroups, so that all of them run at once?
   FA_HD bool one_round(int x) const { return items_of(x) <= wgs_of(x); }
-  // item number i of XCD x (0 <= i < items_of(x))
-  FA_HD Item item(int x, int64_t i) const {
-    int unit, g, rank;  // rank: position of the query tile in the order items are listed
-    if (n_units >= 8) {
-      const int units_x = (n_units - x + 7) / 8;
-      int64_t m;
-      if (causal && one_round(x)) {
-        // every item of the XCD runs at once: the longest query tiles first across its units
-        rank = (int)(i / ((int64_t)units_x * group));
-        const int64_t rest = i % ((int64_t)units_x * group);
-        m = rest / group;
-        g = (int)(rest % group);
-      } else if (causal) {
-        // unit by unit (the XCD's workgroups stream one unit's K/V together, which its L2 holds),
-        // and within a unit the longest query tiles first, all query heads of the group at each
-        m = i / ((int64_t)group * n_qt);
-        const int64_t rest = i % ((int64_t)group * n_qt);
-        rank = (int)(rest / group);
-        g = (int)(rest % group);
-      } else {
-        m = i / ((int64_t)group * n_qt);
-        const int64_t rest = i % ((int64_t)group * n_qt);
-        g = (int)(rest / n_qt);
-        rank = (int)(rest % n_qt);
-      }
-      unit = x + 8 * (int)m;
-    } else {
-      const int s = xcd_share();
-      unit = x / s;
-      const int64_t f = x % s + i * s;
-      if (causal) {
-        rank = (int)(f / group);
-        g = (int)(f % group);
-      } else {
-        g = (int)(f / n_qt);
-        rank = (int)(f % n_qt);
-      }
-    }
+
+  FA_HD Item make(int unit, int g, int t) const {
     Item it;
     it.b = unit / hkv;
     it.h = (unit % hkv) * group + g;
-    it.qt = causal ? n_qt - 1 - rank : rank;
+    it.qt = causal ? n_qt - 1 - t : t;  // t is the rank (longest first) under the causal mask
     return it;
+  }
+  // entry e of the leftover list of XCD x's sequence
+  FA_HD Item left_item(int x, int64_t e) const {
+    const int base = 8 * whole();
+    if (shared_rest()) {
+      const int unit = base + x / share();
+      return causal ? make(unit, (int)(e % group), (int)(e / group)) : make(unit, (int)(e / n_qt), (int)(e % n_qt));
+    }
+    if (causal) {
+      const int64_t per_rank = (int64_t)rest() * group;
+      const int64_t r = e % per_rank;
+      return make(base + (int)(r / group), (int)(r % group), (int)(e / per_rank));
+    }
+    const int64_t r = e % per_unit();
+    return make(base + (int)(e / per_unit()), (int)(r / n_qt), (int)(r % n_qt));
+  }
+  // whole-unit item i of XCD x (0 <= i < n_whole_of()), unit by unit
+  FA_HD Item whole_item(int x, int64_t i) const {
+    const int m = (int)(i / per_unit());
+    const int64_t r = i % per_unit();
+    return causal ? make(x + 8 * m, (int)(r % group), (int)(r / group)) : make(x + 8 * m, (int)(r / n_qt), (int)(r % n_qt));
+  }
+  // causal: items of XCD x whose rank is below t (the whole units' and the leftover ones)
+  FA_HD int64_t rank_prefix(int x, int t) const {
+    const int64_t per_rank = shared_rest() ? group : (int64_t)rest() * group;
+    return (int64_t)t * whole() * group + (rest() ? lo_count_below(x, (int64_t)t * per_rank) : 0);
+  }
+  // item number i of XCD x (0 <= i < items_of(x))
+  FA_HD Item item(int x, int64_t i) const {
+    const int64_t nw = n_whole_of();
+    if (!causal) {
+      if (i < nw) return whole_item(x, i);
+      const int64_t k = i - nw;
+      if (shared_rest()) return left_item(x, lo_entry(x, k));
+      const int64_t L = lo_len();
+      return left_item(x, x * (L / 8) + (x < L % 8 ? x : L % 8) + k);  // x's contiguous run
+    }
+    if (one_round(x)) {
+      // longest first over all of the XCD's items: the rank is the largest t with rank_prefix <= i
+      int lo = 0, hi = n_qt - 1;
+      while (lo < hi) {
+        const int mid = lo + (hi - lo + 1) / 2;
+        if (rank_prefix(x, mid) <= i)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      const int64_t off = i - rank_prefix(x, lo);
+      const int64_t wg = (int64_t)whole() * group;
+      if (off < wg) return make(x + 8 * (int)(off / group), (int)(off % group), lo);
+      const int64_t per_rank = shared_rest() ? group : (int64_t)rest() * group;
+      const int64_t k = lo_count_below(x, (int64_t)lo * per_rank) + (off - wg);
+      return left_item(x, lo_entry(x, k));
+    }
+    const int64_t nl = left_of(x);
+    if (i < nl) return left_item(x, lo_entry(x, i));
+    return whole_item(x, i - nl);
   }
   // position of the XCD's k-th workgroup among its gx workgroups (a bijection of [0, gx))
   FA_HD static int cu_snake(int k, int gx) {

@@ -135,37 +135,48 @@ int main() {
       for (int e = 0; e < 8; ++e) keys.insert(fa::pv_key(ks, lane, e));
     CHECK((int)keys.size() == 16 && *keys.begin() == 16 * ks && *keys.rbegin() == 16 * ks + 15, "pv_key perm");
   }
-  // the work schedule visits every (batch, head, query tile) exactly once, keeps every unit's items
-  // on as few XCDs as its share, and (causal) lists each XCD's items longest first
-  for (int B : {1, 2, 4})
+  // the work schedule visits every (batch, head, query tile) exactly once, keeps each whole unit on
+  // one XCD and each leftover unit with its own share on at most that share, and (causal) lists the
+  // items run at once longest first, or else the leftover items longest first and then each whole
+  // unit's items together, longest first
+  for (int B : {1, 2, 3, 4, 5, 9, 13})
     for (int hkv : {1, 2, 3, 8, 16})
-      for (int group : {1, 4})
+      for (int group : {1, 3, 4})
         for (int n_qt : {1, 3, 8, 17})
           for (int causal = 0; causal < 2; ++causal)
-            for (int grid : {1, 5, 64, 256, 512}) {
+            for (int grid : {1, 5, 64, 256, 512, 768, 1024}) {
               fa::Schedule sc{B * hkv, hkv, group, n_qt, causal != 0, 0};
               const long n_items = (long)B * hkv * group * n_qt;
               sc.grid = sc.choose_grid(grid);
+              CHECK(sc.grid >= 1 && (sc.grid >= 8 || sc.grid >= n_items), "grid leaves an XCD without workgroups");
+              long total = 0;
+              for (int x = 0; x < 8; ++x) {
+                total += sc.items_of(x);
+                CHECK(sc.items_of(x) == 0 || sc.wgs_of(x) > 0, "an XCD holds items but no workgroup");
+              }
+              CHECK(total == n_items, "items per XCD do not add up");
               std::vector<int> seen(n_items, 0);
               std::map<int, std::set<int>> unit_xcds;
               for (int wg = 0; wg < sc.grid; ++wg) {
                 const int x = wg % 8;
-                int prev_qt = 1 << 30;
                 for (long r = 0;; ++r) {
                   const long i = sc.item_index(wg, r);
                   if (i >= sc.items_of(x)) break;
                   const fa::Item it = sc.item(x, i);
                   CHECK(it.b >= 0 && it.b < B && it.h >= 0 && it.h < hkv * group && it.qt >= 0 && it.qt < n_qt,
                         "schedule item out of range");
+                  if (!(it.b >= 0 && it.b < B && it.h >= 0 && it.h < hkv * group && it.qt >= 0 && it.qt < n_qt)) break;
                   seen[((long)it.b * hkv * group + it.h) * n_qt + it.qt]++;
                   unit_xcds[it.b * hkv + it.h / group].insert(x);
-                  (void)prev_qt;
                 }
               }
               for (long k = 0; k < n_items; ++k) CHECK(seen[k] == 1, "schedule misses or repeats an item");
-              for (auto& kv : unit_xcds) CHECK((int)kv.second.size() <= sc.xcd_share(), "unit spread over too many XCDs");
-              // causal: within an XCD, the items run at once are listed longest first; otherwise the
-              // items of one unit are listed together, longest first
+              for (auto& kv : unit_xcds) {
+                if (kv.first < 8 * sc.whole())
+                  CHECK(kv.second.size() == 1 && *kv.second.begin() == kv.first % 8, "whole unit not on its XCD");
+                else if (sc.shared_rest())
+                  CHECK((int)kv.second.size() <= sc.share(), "leftover unit spread beyond its share");
+              }
               if (causal)
                 for (int x = 0; x < 8; ++x) {
                   if (sc.one_round(x)) {
@@ -173,10 +184,16 @@ int main() {
                       CHECK(sc.item(x, i).qt <= sc.item(x, i - 1).qt, "causal items of one round not longest first");
                     continue;
                   }
+                  const long nl = sc.left_of(x);
                   std::set<int> done;
                   for (long i = 1; i < sc.items_of(x); ++i) {
                     const fa::Item a = sc.item(x, i - 1), c = sc.item(x, i);
                     const int ua = a.b * hkv + a.h / group, uc = c.b * hkv + c.h / group;
+                    if (i < nl) {
+                      CHECK(c.qt <= a.qt, "leftover items not longest first");
+                      continue;
+                    }
+                    if (i == nl) continue;  // first whole-unit item
                     if (ua == uc)
                       CHECK(c.qt <= a.qt, "causal items of a unit not longest first");
                     else
@@ -184,6 +201,31 @@ int main() {
                   }
                 }
             }
+  // balance across the XCDs for any number of (batch, kv head) units: with at least four items per
+  // XCD, the most loaded XCD holds at most 10 % more items, and (causal) 10 % more key tiles, than
+  // the mean
+  for (int n_units = 1; n_units <= 64; ++n_units)
+    for (int group : {1, 3, 4})
+      for (int n_qt : {8, 16, 32, 128})
+        for (int causal = 0; causal < 2; ++causal) {
+          if ((long)n_units * group * n_qt < 32) continue;
+          fa::Schedule sc{n_units, 1, group, n_qt, causal != 0, 0};
+          sc.grid = sc.choose_grid(512);
+          double cnt[8] = {0}, work[8] = {0}, mc = 0, mw = 0, xc = 0, xw = 0;
+          for (int x = 0; x < 8; ++x)
+            for (long i = 0; i < sc.items_of(x); ++i) {
+              cnt[x] += 1;
+              work[x] += causal ? sc.item(x, i).qt + 1 : n_qt;
+            }
+          for (int x = 0; x < 8; ++x) {
+            mc += cnt[x] / 8;
+            mw += work[x] / 8;
+            xc = xc > cnt[x] ? xc : cnt[x];
+            xw = xw > work[x] ? xw : work[x];
+          }
+          CHECK(xc <= 1.1 * mc && xw <= 1.1 * mw, "XCD imbalance: %d units, group %d, %d query tiles, causal %d: "
+                "items %.0f / %.2f, work %.0f / %.2f", n_units, group, n_qt, causal, xc, mc, xw, mw);
+        }
   // causal balance of the workload of 4 batches x 16 heads x 8 query tiles (2..16 key tiles each)
   // on 2 resident workgroups per CU: every CU gets the same total
   {
