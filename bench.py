@@ -16,10 +16,15 @@ Prints ONE JSON line. Extra objects:
                   kernel (with `frac_clock_adjusted`, the fraction of the peak at that clock), both
                   from committed rocprofv3 counters when they were taken on the current kernel
                   sources, else null.
-  cpu_baseline  - the float64 CPU oracle timed on this host's cores on the same workload.
+  workloads     - every named workload (the tiny one, the benchmark shape, the strided D=64 one, the
+                  peaked D=256 one and the long GQA one), per mask: time per launch from HIP events,
+                  TFLOP/s, fraction of the peak, algorithmic TB/s (Q, K, V read once, O and LSE written
+                  once) and, where committed counters match the kernel sources, the clock-adjusted fraction.
+  cpu_baseline  - the float64 CPU oracle timed on this host's cores on the same workload, with the host's
+                  core count, the cores this process may use and the worker cap.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                      [--no-backward]
+                      [--no-backward] [--no-workloads]
        python bench.py --sweep | --sweep-backward   (throughput over a fixed list of shapes instead)
 """
 from __future__ import annotations
@@ -38,7 +43,10 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # MI355X dense MFMA, published
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["scaled_dot_product_fa2_amd/csrc/fa_fwd_kernel.h", "scaled_dot_product_fa2_amd/csrc/fa_layout.h",
+                  "scaled_dot_product_fa2_amd/csrc/fa_launch.h", "scaled_dot_product_fa2_amd/csrc/fa_fwd_inst.hip",
                   "scaled_dot_product_fa2_amd/csrc/fa_api.hip"]
+# host processes of the CPU oracle baseline: one BLAS thread each, at most this many
+CPU_WORKER_CAP = 16
 
 
 def kernel_sha() -> str:
@@ -81,7 +89,8 @@ def cpu_baseline(w, q, k, v, outs):
     with the GPU outputs it reproduces."""
     import numpy as np
     import oracle
-    workers = min(16, len(os.sched_getaffinity(0)))
+    affinity = len(os.sched_getaffinity(0))
+    workers = min(CPU_WORKER_CAP, affinity)
     qn, kn, vn = (t.float().numpy() for t in (q, k, v))
     scale = float(np.float32(w.scale))
     total_flop, t_total, worst_o, worst_l = 0.0, 0.0, 0.0, 0.0
@@ -99,6 +108,8 @@ def cpu_baseline(w, q, k, v, outs):
     return {"value": total_flop / t_total / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
             "sample": f"the whole workload, every (batch, head) in both modes; float64 numpy, one BLAS thread "
                       f"per worker; {t_total:.2f} s wall",
+            "host_cpu_count": os.cpu_count(), "affinity_cores": affinity, "worker_cap": CPU_WORKER_CAP,
+            "blas_threads_per_worker": 1,
             "seconds": round(t_total, 3), "gpu_vs_oracle": {"o_err_ratio_max": round(worst_o, 4),
                                                           "lse_abs_err_max": worst_l}}
 
@@ -136,10 +147,57 @@ def backward_timing(w, q, k, v, outs, modes, steps, stream):
     return {"metric": "attention bwd TFLOP/s (five products: 10*B*Hq*Nq*Nkv*D, halved for causal)", "per_mode": res}
 
 
+def workload_timing(name, stream, min_ms=40.0):
+    """Forward throughput of one named workload on its own seeded inputs, per mask: HIP events around
+    back-to-back launches on the launch stream (enough launches for about `min_ms` of kernels) after a
+    warm-up of as many launches again."""
+    import torch
+    import workloads
+    import scaled_dot_product_fa2_amd as fa
+    w = workloads.WORKLOADS[name]
+    dev = stream.device
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    o = torch.empty(w.B, w.Hq, w.Nq, w.D, dtype=w.dtype, device=dev)
+    lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=dev)
+    peak = PEAK_TFLOPS[w.dtype_name]
+    res = {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.Nq, "D": w.D, "dtype": w.dtype_name, "kv_storage": w.kv_layout,
+           "seed": w.seed}
+    for c in w.causal_modes:
+        call = fa.fa_fwd_call(q, k, v, o, lse, causal=c, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps = int(max(10, min(2000, min_ms / max(e0.elapsed_time(e1), 1e-3))))
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = flop(w, c) / (ms / 1e3) / 1e12
+        mode = "causal" if c else "non_causal"
+        sclk = load_profile(w.name, mode, "sclk_mhz")
+        res[mode] = {"ms_per_launch": round(ms, 5), "launches": reps, "tflops": round(tf, 2),
+                     "frac_of_peak": round(tf / peak, 4),
+                     "algorithmic_tb_per_s": round(algorithmic_bytes(w) / (ms / 1e3) / 1e12, 3),
+                     "sclk_mhz": sclk,
+                     "frac_clock_adjusted": round(tf / (peak * sclk / 2400.0), 4) if sclk else None}
+    del q, k, v, o, lse
+    return res
+
+
 # Shapes of the throughput sweep (bf16; 65 536 tokens per head for the first two groups).
 SWEEP_FWD = ([(max(1, 65536 // n), 32, 32, n, 64) for n in (512, 1024, 2048, 4096, 8192, 16384)] +
              [(max(1, 65536 // n), 16, 16, n, 128) for n in (512, 1024, 2048, 4096, 8192, 16384)] +
-             [(1, 32, 8, 16384, 128), (2, 16, 16, 4096, 256), (2, 16, 16, 16384, 256)])
+             [(1, 32, 8, 16384, 128), (2, 16, 16, 4096, 256), (2, 16, 16, 16384, 256)] +
+             # (batch, kv head) unit counts that are not a multiple of the 8 XCDs, beside ones that are
+             [(1, 40, 5, 16384, 128), (1, 64, 8, 16384, 128), (9, 8, 1, 8192, 128), (8, 8, 1, 8192, 128)])
 SWEEP_BWD = [(4, 16, 16, 1024, 128), (4, 16, 16, 4096, 128), (16, 16, 16, 4096, 128), (4, 16, 16, 16384, 128),
              (1, 32, 8, 16384, 128)]
 
@@ -195,6 +253,8 @@ def main():
     ap.add_argument("--workload", default="b4h16n1024d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-workload forward timings of the five named workloads")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark: forward TFLOP/s over a fixed list of shapes, one JSON line each")
     ap.add_argument("--sweep-backward", action="store_true", help="the same for the backward (five-product TFLOP/s)")
@@ -302,6 +362,9 @@ def main():
     }
     if not args.no_backward:
         result["backward"] = backward_timing(w, qd, kd, vd, outs, modes, max(5, min(args.steps, 50)), stream)
+    if not args.no_workloads:
+        # every named workload, timed on its own after the headline's timed region
+        result["workloads"] = {name: workload_timing(name, stream) for name in workloads.WORKLOADS}
     if not args.no_cpu_baseline:
         outs_cpu = {c: (outs[c][0].cpu(), outs[c][1].cpu()) for c in modes}
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, outs_cpu)
