@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 /* Element types of Q, K, V and O (all four share one type). */
 #define FA_DTYPE_F16 0
@@ -49,7 +49,9 @@ extern "C" {
 #define FA_ERR_LAYOUT -6    /* a d-stride is not 1, a base address or b/h/n stride is not 16-byte aligned,
                                a stride is negative, the n-stride exceeds 2^22, or O has a zero stride */
 #define FA_ERR_SCALE -7     /* scale is not a finite number > 0 */
-#define FA_ERR_HIP -8       /* the kernel launch failed (hipGetLastError after the launch) */
+#define FA_ERR_HIP -8       /* the kernel launch failed (hipGetLastError after the launch), or a HIP
+                               query of fa_bwd_noalloc's set-up failed */
+#define FA_ERR_SCRATCH -9   /* fa_bwd_noalloc: B * Hq * Nq exceeds FA_NOALLOC_MAX_ROWS */
 
 /*
  * fa_fwd - enqueue one attention forward on `stream` and return.
@@ -205,6 +207,31 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
                   const int64_t o_stride[3], const int64_t do_stride[3], const int64_t dq_stride[3],
                   const int64_t dk_stride[3], const int64_t dv_stride[3],
                   float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_bwd_noalloc - fa_bwd without the caller's Delta workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. The arguments, validation, results and kernels are those of fa_bwd without `delta`;
+ * Delta is kept instead in a fixed device array of FA_NOALLOC_MAX_ROWS floats (16 MiB) inside the
+ * library, which every GPU the library runs this on holds until the process ends. The entry point
+ * itself allocates nothing: on its first call on a device it looks up that device's copy of the
+ * array (hipStreamGetDevice, hipGetSymbolAddress) and remembers it.
+ *
+ * Limit: B * Hq * Nq <= FA_NOALLOC_MAX_ROWS, else FA_ERR_SCRATCH (checked after the other
+ * validation, before any HIP call, nothing enqueued).
+ * Sharing: all calls on one GPU use that GPU's single array, which keeps the last call's Delta.
+ * Calls that overlap in time on one GPU (on different streams, or from several threads without
+ * ordering) race on it and must not be issued; calls ordered on one stream are safe. Every Delta
+ * row a call reads is written by the same call first, so nothing needs clearing between calls.
+ */
+#define FA_NOALLOC_MAX_ROWS 4194304
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv,
+                   int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                   const int64_t q_stride[4], const int64_t k_stride[4], const int64_t v_stride[4],
+                   const int64_t o_stride[4], const int64_t do_stride[4], const int64_t dq_stride[4],
+                   const int64_t dk_stride[4], const int64_t dv_stride[4],
+                   float scale, int causal, int dtype, void* stream);
 
 /* Launch plan of fa_fwd for a shape, computed on the host without any HIP call. */
 typedef struct fa_plan {

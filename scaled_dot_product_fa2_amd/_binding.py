@@ -11,6 +11,7 @@ import torch
 
 FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
+FA_NOALLOC_MAX_ROWS = 4194304  # fa_bwd_noalloc: largest B * Hq * Nq (its fixed Delta array)
 _DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +55,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                            i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f32, i32, i32, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                   i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f32, i32, i32, vp]
+    lib.fa_bwd_noalloc.restype = i32
     lib.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                   i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f32, i64, i64, i32, vp]
     lib.fa_bwd_window.restype = i32
@@ -247,6 +251,36 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
                                             ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return dq, dk, dv
+
+
+def fa_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                   dout: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, *, causal: bool = False,
+                   scale: Optional[float] = None, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """``fa_bwd`` through the entry point that allocates nothing: Delta lives in the library's fixed
+    per-GPU array (B * Hq * Nq <= FA_NOALLOC_MAX_ROWS), so no workspace is passed, and dq, dk, dv must
+    be given. Calls that overlap in time on one GPU share that array and must not be issued."""
+    if not q.is_cuda:
+        raise ValueError("all tensors must be on the GPU")
+    _on_device(q.device, k=k, v=v, o=o, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv)
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v, o, dout must share one dtype, float16 or bfloat16")
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nkv, _ = k.shape
+    if k.shape != (B, Hkv, Nkv, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, o and dout")
+    if lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, Hq, Nq) tensor")
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{name} must match the shape and dtype of its input")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    stream = _stream_for(q.device, stream)
+    _check(load_library().fa_bwd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v),
+        _strides(o), _strides(dout), _strides(dq), _strides(dk), _strides(dv), float(scale), int(bool(causal)),
+        _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream)))
 
 
 def fa_fwd_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, window_left: int = -1,

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_launch.h"
@@ -166,6 +167,35 @@ int launch_bwd_d(int64_t D, const fa::BwdParams& p, hipStream_t stream) {
   }
 }
 
+// ---- fa_bwd_noalloc: Delta in a fixed device array instead of a caller workspace. Each GPU holds
+// its own copy at its own address; host code must use that address (looked up once per device with
+// hipGetSymbolAddress), never the array's name, which on the host is only a stand-in.
+static __device__ __align__(256) float scratch[FA_NOALLOC_MAX_ROWS];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device that `stream` belongs to (the current device for the
+// null stream); nullptr on a HIP error.
+float* scratch_for(hipStream_t stream) {
+  int dev = -1;
+  const hipError_t qe = stream == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(stream, &dev);
+  if (qe != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return nullptr;
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (prev != dev && hipSetDevice(prev) != hipSuccess) return nullptr;
+    if (e != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,6 +215,8 @@ const char* fa_strerror(int code) {
              "no zero output strides)";
     case FA_ERR_SCALE: return "scale must be a finite number > 0";
     case FA_ERR_HIP: return "HIP kernel launch failed";
+    case FA_ERR_SCRATCH:
+      return "fa_bwd_noalloc: B * Hq * Nq exceeds the fixed Delta array of FA_NOALLOC_MAX_ROWS (4194304) rows";
     default: return "unknown error code";
   }
 }
@@ -398,6 +430,29 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int causal, int dtype, void* stream) {
   return bwd_entry(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride,
                    o_stride, do_stride, dq_stride, dk_stride, dv_stride, scale, causal, false, -1, -1, dtype, stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv,
+                   int64_t D, const int64_t q_stride[4], const int64_t k_stride[4], const int64_t v_stride[4],
+                   const int64_t o_stride[4], const int64_t do_stride[4], const int64_t dq_stride[4],
+                   const int64_t dk_stride[4], const int64_t dv_stride[4], float scale, int causal, int dtype,
+                   void* stream) {
+  // validate as fa_bwd does, with a placeholder (non-null, aligned) workspace pointer
+  fa::BwdParams p;
+  float* const placeholder = reinterpret_cast<float*>(uintptr_t(256));
+  int rc = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, placeholder, B, Hq, Hkv, Nq, Nkv, D, q_stride, k_stride,
+                       v_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride, scale, causal != 0, dtype, &p);
+  if (rc != FA_OK) return rc;
+  if (B * Hq * Nq > (int64_t)FA_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH;  // no overflow: check_shape bounds it
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* const delta = scratch_for(s);
+  if (delta == nullptr) return FA_ERR_HIP;
+  p.delta = delta;
+  const bool cz = causal != 0;
+  if (dtype == FA_DTYPE_BF16)
+    return cz ? launch_bwd_d<__bf16, true>(D, p, s) : launch_bwd_d<__bf16, false>(D, p, s);
+  return cz ? launch_bwd_d<_Float16, true>(D, p, s) : launch_bwd_d<_Float16, false>(D, p, s);
 }
 
 int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

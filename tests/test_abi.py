@@ -183,6 +183,37 @@ def test_bwd_validation_rejects(name, over, code):
     assert _bwd_call(**over) == D_[code]
 
 
+def _bwd_noalloc_call(**over):
+    a = dict(BWD_VALID)
+    a.update(over)
+    lib = _lib()
+    st = [(_st(*a[n]) if a[n] else None) for n in ("qs", "ks", "vs", "os", "dos", "dqs", "dks", "dvs")]
+    return lib.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                              a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["D"], *st, a["scale"], a["causal"],
+                              a["dtype"], None)
+
+
+def _noalloc_over_limit():
+    """A shape one query row per head past the fixed Delta array (B * Hq * Nq = max + 2)."""
+    nq = D_["FA_NOALLOC_MAX_ROWS"] // 2 + 1
+    qs = (2 * nq * 64, nq * 64, 64, 1)
+    return dict(B=1, Hq=2, Hkv=1, Nq=nq, Nkv=128, qs=qs, os=qs, dos=qs, dqs=qs)
+
+
+@pytest.mark.parametrize("name,over,code", [b for b in BWD_BAD if "delta" not in b[0]] +
+                         [("over_scratch", _noalloc_over_limit(), "FA_ERR_SCRATCH")],
+                         ids=[b[0] for b in BWD_BAD if "delta" not in b[0]] + ["over_scratch"])
+def test_bwd_noalloc_validation_rejects(name, over, code):
+    """The no-allocation backward validates like fa_bwd, then rejects a Delta larger than its fixed array,
+    all before any HIP call."""
+    assert _bwd_noalloc_call(**over) == D_[code]
+
+
+def test_noalloc_limit_matches_binding():
+    from scaled_dot_product_fa2_amd import _binding
+    assert _binding.FA_NOALLOC_MAX_ROWS == D_["FA_NOALLOC_MAX_ROWS"]
+
+
 def _bwd_win_call(left, right, **over):
     a = dict(BWD_VALID)
     a.update(over)
