@@ -95,13 +95,6 @@ constexpr int kBwdLead = 3;
 // fragment less read-ahead there keeps it inside the register file.
 constexpr int kBwdDqMaskedLead = 2;
 
-// Compile-time part of the row-fragment read of rows 32*qb + (lane % 32), chunk 2*s + lane/32, of a
-// tile in the transposing (unswizzled) layout; the per-lane part depends on s only through its parity.
-template <int D, int ROWS>
-FA_HD int q_const(int qb, int s) {
-  return (2 * s / chunks_per_seg<D>()) * (ROWS * seg_bytes<D>()) + 32 * qb * seg_bytes<D>();
-}
-
 // Delta_i = sum_d O_id * dO_id for every (batch, head, row), fp32. D/8 lanes per row, one
 // 16-byte vector of O and of dO per lane, then a butterfly sum over those lanes.
 template <typename T, int D>
@@ -231,8 +224,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const int per_head = qt_end - qt0;
   const int n_work = p.group * per_head;
   const int q_stride = (int)(p.q_sn * 2), o_stride = (int)(p.do_sn * 2);
-  const int q_dma_off = (int)dma_lane_offset<D, true>(lane, q_stride);
-  const int o_dma_off = (int)dma_lane_offset<D, true>(lane, o_stride);
+  const int q_dma_off = (int)dma_lane_offset<D, false>(lane, q_stride);
+  const int o_dma_off = (int)dma_lane_offset<D, false>(lane, o_stride);
 
   auto issue = [&](int w, lds_char_t* qt, lds_char_t* ot, float* ls, float* dl) {
     const int h = kvh * p.group + w / per_head;
@@ -261,14 +254,15 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     }
   };
 
-  // per-lane parts of the tile reads: row fragments of the Q/dO tiles (transposing layout, so the
-  // chunk slot is not swizzled) and the transposing reads
+  // per-lane parts of the tile reads. The Q and dO tiles are read as row fragments and transposed;
+  // both kinds of read are free of bank conflicts on the swizzled layout (fa_layout.h).
   constexpr int KP = kfrag_parities<D>();
   int q_lane[KP];
 #pragma unroll
-  for (int par = 0; par < KP; ++par) q_lane[par] = tile_chunk_offset<D, BQ, true>(lane & 31, 2 * par + (lane >> 5));
-  const int t_lane = vtr_lane_offset<D, BQ>(lane);
+  for (int par = 0; par < KP; ++par) q_lane[par] = kfrag_lane_offset<D, BQ>(par, lane);
+  const int t_lane[2] = {vtr_swz_lane_offset<D, BQ>(0, lane), vtr_swz_lane_offset<D, BQ>(1, lane)};
   const float c = p.c;
+
   auto step = [&](auto stage_c, int w) {
     constexpr int S = decltype(stage_c)::value;
     lds_char_t* const qt = (lds_char_t*)(S == 0 ? q_st0_raw : q_st1_raw);
@@ -297,7 +291,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
         vec8 qa[NS], oa[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const int off = q_lane[s % KP] + q_const<D, BQ>(qb, s);
+          const int off = q_lane[s % KP] + kfrag_const_offset<D, BQ>(qb, s);
           qa[s] = __builtin_bit_cast(vec8, lds_read16(qt + off));
           if (DO_K) oa[s] = __builtin_bit_cast(vec8, lds_read16(ot + off));
         }
@@ -344,12 +338,12 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           for (int db = 0; db < NDB; ++db) {
             i16x4 olo{}, ohi{}, qlo{}, qhi{};
             if (DO_V) {
-              olo = lds_read_tr(ot + t_lane + vtr_const_offset<D, BQ>(2 * qb + ks, 0, db));
-              ohi = lds_read_tr(ot + t_lane + vtr_const_offset<D, BQ>(2 * qb + ks, 1, db));
+              olo = lds_read_tr(ot + t_lane[0] + vtr_swz_const_offset<D, BQ>(2 * qb + ks, db));
+              ohi = lds_read_tr(ot + t_lane[1] + vtr_swz_const_offset<D, BQ>(2 * qb + ks, db));
             }
             if (DO_K) {
-              qlo = lds_read_tr(qt + t_lane + vtr_const_offset<D, BQ>(2 * qb + ks, 0, db));
-              qhi = lds_read_tr(qt + t_lane + vtr_const_offset<D, BQ>(2 * qb + ks, 1, db));
+              qlo = lds_read_tr(qt + t_lane[0] + vtr_swz_const_offset<D, BQ>(2 * qb + ks, db));
+              qhi = lds_read_tr(qt + t_lane[1] + vtr_swz_const_offset<D, BQ>(2 * qb + ks, db));
             }
             if (DPAD && ((lane >> 4) & 1)) {
               olo = i16x4{};
@@ -482,7 +476,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const char* kbase = (const char*)p.k + (b * p.k_sb + kvh * p.k_sh + (int64_t)sq.k_tok0 * p.k_sn) * 2;
   const char* vbase = (const char*)p.v + (b * p.v_sb + kvh * p.v_sh + (int64_t)sq.k_tok0 * p.v_sn) * 2;
   const int k_stride = (int)(p.k_sn * 2), v_stride = (int)(p.v_sn * 2);
-  const int k_dma_off = (int)dma_lane_offset<D, true>(lane, k_stride);
+  const int k_dma_off = (int)dma_lane_offset<D, false>(lane, k_stride);
   const int v_dma_off = (int)dma_lane_offset<D, false>(lane, v_stride);
   // key tiles this workgroup visits: [t0, t0 + n_tiles)
   int t0 = 0, n_tiles;
@@ -497,14 +491,13 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const int wq_last = wq0 + 31;
   const float c = p.c;
 
+  // per-lane parts of the tile reads: K and V row fragments (both tiles swizzled), and the
+  // transposing reads of the K tile, conflict-free on the swizzled layout as well (fa_layout.h)
   constexpr int KP = kfrag_parities<D>();
-  int v_lane[KP], k_lane[KP];
+  int frag_lane[KP];
 #pragma unroll
-  for (int par = 0; par < KP; ++par) {
-    v_lane[par] = kfrag_lane_offset<D, BKV>(par, lane);
-    k_lane[par] = tile_chunk_offset<D, BKV, true>(lane & 31, 2 * par + half);
-  }
-  const int kt_lane = vtr_lane_offset<D, BKV>(lane);
+  for (int par = 0; par < KP; ++par) frag_lane[par] = kfrag_lane_offset<D, BKV>(par, lane);
+  const int kt_lane[2] = {vtr_swz_lane_offset<D, BKV>(0, lane), vtr_swz_lane_offset<D, BKV>(1, lane)};
 
   auto step = [&](auto stage_c, int j) {
     constexpr int S = decltype(stage_c)::value;
@@ -533,8 +526,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          ka[s][kb] = __builtin_bit_cast(vec8, lds_read16(kt + k_lane[s % KP] + q_const<D, BKV>(kb, s)));
-          va[s][kb] = __builtin_bit_cast(vec8, lds_read16(vt + v_lane[s % KP] + kfrag_const_offset<D, BKV>(kb, s)));
+          ka[s][kb] = __builtin_bit_cast(vec8, lds_read16(kt + frag_lane[s % KP] + kfrag_const_offset<D, BKV>(kb, s)));
+          va[s][kb] = __builtin_bit_cast(vec8, lds_read16(vt + frag_lane[s % KP] + kfrag_const_offset<D, BKV>(kb, s)));
         }
 #pragma unroll
       for (int s = 0; s < NS; ++s)
@@ -587,8 +580,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          i16x4 lo = lds_read_tr(kt + kt_lane + vtr_const_offset<D, BKV>(ks, 0, db));
-          i16x4 hi = lds_read_tr(kt + kt_lane + vtr_const_offset<D, BKV>(ks, 1, db));
+          i16x4 lo = lds_read_tr(kt + kt_lane[0] + vtr_swz_const_offset<D, BKV>(ks, db));
+          i16x4 hi = lds_read_tr(kt + kt_lane[1] + vtr_swz_const_offset<D, BKV>(ks, db));
           if (DPAD && ((lane >> 4) & 1)) {
             lo = i16x4{};
             hi = i16x4{};

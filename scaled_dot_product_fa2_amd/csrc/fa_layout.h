@@ -161,6 +161,21 @@ FA_HD int vtr_const_offset(int ks, int half, int db) {
   return (16 * ks + 8 * half) * seg_bytes<D>() + db * (ROWS * seg_bytes<D>());
 }
 
+// Transposing reads of a swizzled row tile, i.e. a tile that is read both as MFMA row fragments
+// (16 bytes per lane, conflict-free only with the swizzle) and transposed (the backward's Q, dO
+// and K tiles). The rows of one transposing read lie in one 256-byte line, which shares a single
+// swizzle value, so the read stays conflict-free; the swizzle depends on the read's half but not on
+// its key slice or head-dim block. Offset = per-lane part for the half + compile-time part.
+template <int D, int ROWS>
+FA_HD int vtr_swz_lane_offset(int half, int lane) {
+  const int row = vtr_row(0, half, lane), col = vtr_col_clamped<D>(0, lane);
+  return tile_chunk_offset<D, ROWS, false>(row, col / 8) + (col % 8) * 2;
+}
+template <int D, int ROWS>
+FA_HD int vtr_swz_const_offset(int ks, int db) {
+  return 16 * ks * seg_bytes<D>() + db * (ROWS * seg_bytes<D>());
+}
+
 // Key tiles a query tile [q0, q0 + bq) visits: all of [0, Nkv) without the mask;
 // with the top-left causal mask only keys <= the tile's last row.
 FA_HD int64_t kv_tiles_for_qtile(int64_t q0, int64_t bq, int64_t nkv, int64_t bkv, bool causal) {

@@ -115,7 +115,71 @@ void check_d() {
       }
 }
 
+// Transposing reads of a swizzled tile (read as row fragments as well): the same operand elements
+// as from the unswizzled layout, and no bank conflicts for either kind of read.
+template <int D, int ROWS>
+void check_swizzled_transpose() {
+  std::vector<Elt> lds = dma_image<D, ROWS, false>();
+  const int NDB = D < 32 ? 1 : D / 32;
+  for (int db = 0; db < NDB; ++db)
+    for (int ks = 0; ks < ROWS / 16; ++ks)
+      for (int half = 0; half < 2; ++half) {
+        int addr[64];
+        for (int lane = 0; lane < 64; ++lane) {
+          const int row = fa::vtr_row(ks, half, lane), col = fa::vtr_col_clamped<D>(db, lane);
+          addr[lane] = fa::tile_chunk_offset<D, ROWS, false>(row, col / 8) + (col % 8) * 2;
+          const int split = fa::vtr_swz_lane_offset<D, ROWS>(half, lane) + fa::vtr_swz_const_offset<D, ROWS>(ks, db);
+          CHECK(addr[lane] == split, "swizzled tr offset split D=%d ROWS=%d", D, ROWS);
+          CHECK(addr[lane] % 8 == 0 && addr[lane] >= 0 && addr[lane] + 8 <= ROWS * D * 2, "swizzled tr addr D=%d", D);
+        }
+        for (int lane = 0; lane < 64; ++lane) {
+          if (D < 32 && ((lane >> 4) & 1)) continue;  // padding lanes are zeroed by the kernel
+          for (int e = 0; e < 4; ++e) {
+            const int src = 16 * (lane / 16) + 4 * e + (lane % 16) / 4;
+            const Elt x = lds[addr[src] / 2 + (lane % 4)];
+            CHECK(x.row == fa::pv_key(ks, lane, 4 * half + e) && x.col == 32 * db + lane % 32,
+                  "swizzled tr operand D=%d ROWS=%d", D, ROWS);
+          }
+        }
+        for (int span = 16; span <= (D >= 32 ? 32 : 16); span *= 2)
+          for (int g0 = 0; g0 < 64; g0 += span) {
+            std::set<int> slots, chunks;
+            for (int lane = g0; lane < g0 + span; ++lane) {
+              chunks.insert(addr[lane] / 16);
+              slots.insert((addr[lane] / 16) % 16);
+            }
+            CHECK(slots.size() == chunks.size(), "swizzled tr read bank conflict D=%d ROWS=%d span=%d", D, ROWS, span);
+          }
+      }
+  // and its row fragments through the swizzled fragment offsets
+  for (int kb = 0; kb < ROWS / 32; ++kb)
+    for (int s = 0; s < D / 16; ++s) {
+      for (int lane = 0; lane < 64; ++lane) {
+        const int byte = fa::kfrag_lane_offset<D, ROWS>(s % fa::kfrag_parities<D>(), lane) +
+                         fa::kfrag_const_offset<D, ROWS>(kb, s);
+        for (int e = 0; e < 8; ++e) {
+          const Elt x = lds[byte / 2 + e];
+          CHECK(x.row == 32 * kb + lane % 32 && x.col == 16 * s + 8 * (lane / 32) + e, "row frag D=%d ROWS=%d", D, ROWS);
+        }
+      }
+      for (int ph = 0; ph < 4; ++ph) {
+        std::set<int> slots;
+        for (int lane = 16 * ph; lane < 16 * ph + 16; ++lane)
+          slots.insert(((fa::kfrag_lane_offset<D, ROWS>(s % fa::kfrag_parities<D>(), lane) +
+                         fa::kfrag_const_offset<D, ROWS>(kb, s)) / 16) % 16);
+        CHECK(slots.size() == 16, "row frag bank conflict D=%d ROWS=%d", D, ROWS);
+      }
+    }
+}
+
 int main() {
+  check_swizzled_transpose<16, 64>();
+  check_swizzled_transpose<32, 64>();
+  check_swizzled_transpose<64, 64>();
+  check_swizzled_transpose<128, 64>();
+  check_swizzled_transpose<256, 64>();
+  check_swizzled_transpose<256, 32>();
+  check_swizzled_transpose<128, 32>();
   check_d<16>();
   check_d<32>();
   check_d<64>();
