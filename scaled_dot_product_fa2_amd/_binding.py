@@ -159,6 +159,40 @@ def fa_fwd_call(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
     return FaCall(args, (q, k, v, out, lse, strides))
 
 
+class FaBwdCall:
+    """A validated, pre-marshalled fa_bwd call on fixed tensors: calling it enqueues one backward
+    (its three kernels). Built by ``fa_bwd_call``; the tensors must stay alive while it is used."""
+
+    def __init__(self, args, keepalive):
+        self._fn = load_library().fa_bwd
+        self._args = args
+        self._keepalive = keepalive
+
+    def __call__(self) -> None:
+        code = self._fn(*self._args)
+        if code != 0:
+            raise FaError(code, fa_strerror(code))
+
+
+def fa_bwd_call(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                dout: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, delta: torch.Tensor, *,
+                causal: bool = False, scale: Optional[float] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> FaBwdCall:
+    """Prepare repeated backwards of the same tensors (see FaBwdCall); checks arguments once."""
+    fa_bwd(q, k, v, o, lse, dout, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv, delta=delta,
+           stream=stream)  # validates and runs once
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nkv, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    stream = _stream_for(q.device, stream)
+    strides = [_strides(t) for t in (q, k, v, o, dout, dq, dk, dv)]
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o, lse, dout, dq, dk, dv, delta)]
+    args = (*ptrs, B, Hq, Hkv, Nq, Nkv, D, *strides, ctypes.c_float(scale), int(bool(causal)), _DTYPES[q.dtype],
+            ctypes.c_void_p(stream.cuda_stream))
+    return FaBwdCall(args, (q, k, v, o, lse, dout, dq, dk, dv, delta, strides))
+
+
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
            lse: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None
