@@ -569,11 +569,21 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       probs(IC<1>());
     else
       probs(IC<0>());
-    vec8 sfr[NKS];
+    // dS enters the dQ product as two terms of the input dtype, hi = round(dS) and lo = round(dS - hi),
+    // so the product sees dS to about twice the dtype's precision: where dQ is a sum of terms that
+    // cancel (keys sharing a large component), one rounding of dS would dominate the result.
+    // The remainder is taken from dS as stored (no multiply-add contraction with the product that
+    // formed it), so every instance, masked or not, rounds the same values.
+    auto ds_terms = [&](int ks, vec8& hi_v, vec8& lo_v) {
+#pragma clang fp contract(off)
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sfr[ks][e] = (T)st[ks >> 1][pv_src_reg(ks, e)];
+      for (int e = 0; e < 8; ++e) {
+        const float x = st[ks >> 1][pv_src_reg(ks, e)];
+        const T hi = (T)x;
+        hi_v[e] = hi;
+        lo_v[e] = (T)(x - (float)hi);
+      }
+    };
     {
       vec8 kT[NKS][NDB];
 #pragma unroll
@@ -589,15 +599,23 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           kT[ks][db] = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+      for (int ks = 0; ks < NKS; ++ks) {
+        vec8 sfr, sfl;
+        ds_terms(ks, sfr, sfl);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) dqT[db] = Elem<T>::mfma(kT[ks][db], sfr[ks], dqT[db]);
+        for (int db = 0; db < NDB; ++db) {
+          dqT[db] = Elem<T>::mfma(kT[ks][db], sfr, dqT[db]);
+          dqT[db] = Elem<T>::mfma(kT[ks][db], sfl, dqT[db]);
+        }
+      }
       constexpr int NF = NKS * NDB;
-      constexpr int LEAD = kBwdLead + 1 < NF ? kBwdLead + 1 : NF;
+      // the window instance at D >= 128 holds the band's bounds as well: less read-ahead there
+      constexpr int LEAD_F = D >= 128 && WINDOW ? kBwdLead : kBwdLead + 1;
+      constexpr int LEAD = LEAD_F < NF ? LEAD_F : NF;
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * LEAD, 0);
 #pragma unroll
       for (int i = 0; i < NF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
         if (i + LEAD < NF) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
     }
