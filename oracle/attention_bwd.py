@@ -43,7 +43,7 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["attention_bwd_ref", "head_bwd_ref", "dq_rows", "attention_varlen_bwd_ref"]
+__all__ = ["attention_bwd_ref", "head_bwd_ref", "dq_rows", "attention_varlen_bwd_ref", "softmax_rows"]
 
 
 def _f64(x) -> np.ndarray:
@@ -53,8 +53,9 @@ def _f64(x) -> np.ndarray:
     return a
 
 
-def _softmax_rows(qh, kh, r, causal, scale, window=None):
-    """P for query rows r of one head: softmax of the scaled scores over the visible keys."""
+def softmax_rows(qh, kh, r, causal, scale, window=None):
+    """P for query rows r of one head: softmax of the scaled scores over the visible keys (the
+    forward definition: scores scale * <q_i, k_j>, top-left causal key set, optional window)."""
     s = scale * (qh[r] @ kh.T)
     key_pos = np.arange(kh.shape[0])
     if causal:
@@ -89,7 +90,7 @@ def head_bwd_ref(qh, kh, vh, doh, *, causal: bool, scale: float,
     rows = np.arange(qh.shape[0])
     for start in range(0, rows.shape[0], row_chunk):
         r = rows[start:start + row_chunk]
-        p = _softmax_rows(qh, kh, r, causal, scale, window)  # recomputed probabilities
+        p = softmax_rows(qh, kh, r, causal, scale, window)  # recomputed probabilities
         o = p @ vh                                       # exact forward output of these rows
         delta = np.sum(o * doh[r], axis=1)               # Delta = rowsum(O * dO)
         dp = doh[r] @ vh.T                               # dP = dO V^T
@@ -143,7 +144,7 @@ def dq_rows(q, k, v, do, b: int, h: int, rows: Sequence[int], *, causal: bool,
     kvh = h // (Hq // Hkv)
     qh, kh, vh = _f64(q[b, h]), _f64(k[b, kvh]), _f64(v[b, kvh])
     r = np.asarray(rows, dtype=np.int64)
-    p = _softmax_rows(qh, kh, r, causal, scale)
+    p = softmax_rows(qh, kh, r, causal, scale)
     doh = _f64(do[b, h])[r]
     delta = np.sum((p @ vh) * doh, axis=1)
     ds = scale * p * (doh @ vh.T - delta[:, None])

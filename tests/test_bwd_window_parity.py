@@ -1,7 +1,8 @@
 """GPU parity of the sliding-window backward (fa_bwd_window) against the float64 backward oracle's
-window mask: every gradient element of every case, with the tolerance of the causal and full
-backward (the roundings are the same; the window only removes terms). A query row whose window
-holds no key has a zero dQ row and adds nothing to dK or dV."""
+window mask: every gradient element of every case, within the elementwise error bound of the
+causal and full backward (tests/grad_bound.py, with the window's visible key set; the roundings are
+the same, the window only removes terms). A query row whose window holds no key has a zero dQ row
+and adds nothing to dK or dV."""
 from __future__ import annotations
 
 import numpy as np
@@ -11,7 +12,8 @@ import torch
 import oracle
 import workloads
 from tests.parity_util import f32_scale, to_f64
-from tests.test_bwd_parity import _dout, _grad_ratio
+from tests import grad_bound as gb
+from tests.test_bwd_parity import _dout, assert_within_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -36,14 +38,12 @@ def _run(B, Hq, Hkv, Nq, Nkv, D, dtype, left, right, seed, scale=None):
     torch.cuda.synchronize()
     win = (None if left < 0 else left, None if right < 0 else right)
     s = f32_scale(scale) if scale is not None else None
+    if s is None:
+        s = f32_scale(1.0 / np.sqrt(D))
     ref = oracle.attention_bwd_ref(to_f64(q), to_f64(k), to_f64(v), to_f64(do), causal=False, scale=s, window=win)
-    floor = 1e-3 * float(np.sqrt(np.mean(to_f64(do) ** 2)))
-    worst = {}
-    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
-        g = to_f64(got)
-        assert np.all(np.isfinite(g)), f"non-finite {name}"
-        worst[name] = _grad_ratio(g, r, dtype, floor=floor)
-    assert max(worst.values()) <= 1.0, f"gradient error ratios {worst}"
+    bounds = gb.attention_bwd_bound(q, k, v, do, o, lse, ref[1], ref[2], causal=False, scale=s, dtype=dtype,
+                                    window=win)
+    worst = assert_within_bound((dq, dk, dv), ref, bounds, f"window ({left},{right}) D{D}")
     # a row whose window holds no key gets an exactly zero dQ row
     rows = np.arange(Nq)
     lo = np.maximum(0, rows - (Nq if left < 0 else left))
@@ -119,19 +119,27 @@ def test_bwd_window_long_sequence_sampled():
     kv0 = r0 - left                      # keys the rows r0..r1 can see start here
     k64, v64 = to_f64(k[:, :, kv0:r1]), to_f64(v[:, :, kv0:r1])
     G = w.Hq // w.Hkv
+    o64, lse64 = to_f64(o[:, :, r0:r1]), to_f64(lse[:, :, r0:r1])
     dk_ref = np.zeros((k1 - k0, w.D))
     dv_ref = np.zeros((k1 - k0, w.D))
+    bk_sum = np.zeros((k1 - k0, w.D))
+    bv_sum = np.zeros((k1 - k0, w.D))
     for h in range(3 * G, 4 * G):
         rq, rk, rv = _bwd_slice(q64[0, h], k64[0, 3], v64[0, 3], do64[0, h], left, sc)
         dk_ref += rk[k0 - kv0:k1 - kv0]
         dv_ref += rv[k0 - kv0:k1 - kv0]
+        bq, bk, bv = gb.head_bwd_bound(q64[0, h], k64[0, 3], v64[0, 3], do64[0, h], o64[0, h], lse64[0, h],
+                                       causal=False, scale=sc, dtype=w.dtype, window=(0, left))
+        bk_sum += bk[k0 - kv0:k1 - kv0]
+        bv_sum += bv[k0 - kv0:k1 - kv0]
         rows = sorted({0, 1, 511, 1023, r1 - r0 - 1, *map(int, rng.integers(0, r1 - r0, 6))})
-        got = to_f64(dq[0, h, r0:r1])[rows]
-        assert _grad_ratio(got[None, None], rq[rows][None, None], w.dtype,
-                           floor=1e-3) <= 1.0, f"h={h}: dq rows"
-    for name, got, r in (("dk", dk[0, 3, k0:k1], dk_ref), ("dv", dv[0, 3, k0:k1], dv_ref)):
-        ratio = _grad_ratio(to_f64(got)[None, None], r[None, None], w.dtype, floor=1e-3)
-        assert ratio <= 1.0, f"{name}: ratio {ratio:.3f}"
+        ratio = gb.bound_ratio(to_f64(dq[0, h, r0:r1])[rows], rq[rows], bq[rows])
+        assert ratio <= 1.0, f"h={h}: dq rows, error / bound {ratio:.3f}"
+    bk_sum, bv_sum = gb.finish_kv(bk_sum, bv_sum, dk_ref, dv_ref, w.dtype)
+    for name, got, r, bnd in (("dk", dk[0, 3, k0:k1], dk_ref, bk_sum), ("dv", dv[0, 3, k0:k1], dv_ref, bv_sum)):
+        ratio = gb.bound_ratio(to_f64(got), r, bnd)
+        print(f"[result] window long sequence {name}: error / bound {ratio:.4f}", flush=True)
+        assert ratio <= 1.0, f"{name}: error / bound {ratio:.3f}"
 
 
 def _bwd_slice(qh, kh, vh, doh, left, scale):

@@ -15,8 +15,8 @@ the float64 oracles with the same tolerances as the other parity tests.
   puts some rows on each side.
 The structured inputs are built in float32 and rounded to the 16-bit dtype once; the oracle sees
 the same rounded tensors. In the monotone cases every key shares a large component, which makes dQ
-a cancelling sum; all three gradients are held to the usual tolerance there, against the exact
-gradient for the forward's stored 16-bit O (which Delta is formed from).
+a cancelling sum; the gradients are held to the same elementwise error bound as everywhere else
+(tests/grad_bound.py).
 """
 from __future__ import annotations
 
@@ -29,7 +29,8 @@ import torch
 import oracle
 import workloads
 from tests import parity_util as pu
-from tests.test_bwd_parity import _dout, _grad_ratio
+from tests import grad_bound as gb
+from tests.test_bwd_parity import _dout, assert_within_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -74,30 +75,13 @@ def test_monotone_scores_forward_and_backward(rising, causal, dtype):
     torch.cuda.synchronize()
     sc = pu.f32_scale(scale)
     q64, k64, v64, do64 = (pu.to_f64(t) for t in (q, k, v, do))
-    rq, rk, rv = oracle.attention_bwd_ref(q64, k64, v64, do64, causal=causal, scale=sc)
-    # The backward's input O is the forward's 16-bit output, and Delta = rowsum(O * dO) is formed
-    # from it. With every key sharing a large component, dQ = dS K amplifies that half-ulp
-    # difference (sum_j dS_ij = -Delta error, times the common component) beyond the rounding
-    # tolerance, so the reference is the exact gradient for the stored O:
-    #   dS' = dS - scale * P * (Delta16 - Delta)  =>  dQ' = dQ - scale * d * (P K),  dK' = dK - scale * P^T (d * Q)
-    # with d = Delta16 - Delta; P K is the oracle forward with V := K, P^T X the oracle's dV for dO := X.
-    o_exact, _ = oracle.attention_ref(q64, k64, v64, causal=causal, scale=sc)
-    d = np.sum(pu.to_f64(o) * do64, axis=-1) - np.sum(o_exact * do64, axis=-1)
-    pk, _ = oracle.attention_ref(q64, k64, k64, causal=causal, scale=sc)
-    _, _, ptdq = oracle.attention_bwd_ref(q64, k64, k64, d[..., None] * q64, causal=causal, scale=sc)
-    ref = (rq - sc * d[..., None] * pk, rk - sc * ptdq, rv)
-    floor = 1e-3 * float(np.sqrt(np.mean(do64 ** 2)))
-    for name, got, r in zip(("dk", "dv"), (dk, dv), ref[1:]):
-        g = pu.to_f64(got)
-        assert np.all(np.isfinite(g)), f"non-finite {name}"
-        ratio = _grad_ratio(g, r, dtype, floor=floor)
-        assert ratio <= 1.0, f"{name}: gradient error ratio {ratio:.3f}"
-    # dQ = scale * sum_j dS_ij k_j, where with every key sharing a large component the terms cancel to a
-    # small result: one rounding of dS to the dtype would dominate it, and the kernel feeds the dQ
-    # product dS as two dtype terms (rounded value and rounded remainder) so that it does not.
-    ratio = _grad_ratio(pu.to_f64(dq), ref[0], dtype, floor=floor)
-    print(f"[result] monotone rising={rising} causal={causal} {dtype}: dq error ratio {ratio:.3f}", flush=True)
-    assert ratio <= 1.0, f"dq: gradient error ratio {ratio:.3f}"
+    refs = oracle.attention_bwd_ref(q64, k64, v64, do64, causal=causal, scale=sc)
+    # With every key sharing a large component dQ = scale sum_j dS_ij k_j is a cancelling sum: one
+    # rounding of dS to the dtype would dominate it (the kernel feeds dS to the dQ product as two
+    # dtype terms), and so does Delta's use of the stored 16-bit O, which the bound accounts for.
+    bounds = gb.attention_bwd_bound(q64, k64, v64, do64, o, lse, refs[1], refs[2], causal=causal, scale=sc,
+                                    dtype=dtype)
+    assert_within_bound((dq, dk, dv), refs, bounds, f"monotone rising={rising} causal={causal} {dtype}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -123,11 +107,11 @@ def test_mqa_32_heads(causal):
     do = _dout(1, 32, 300, 128, torch.bfloat16, 3301)
     dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, lse, do.to(DEV), causal=causal)
     torch.cuda.synchronize()
-    ref = oracle.attention_bwd_ref(pu.to_f64(q), pu.to_f64(k), pu.to_f64(v), pu.to_f64(do), causal=causal,
-                                   scale=pu.f32_scale(1.0 / math.sqrt(128)))
-    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
-        ratio = _grad_ratio(pu.to_f64(got), r, torch.bfloat16)
-        assert ratio <= 1.0, f"{name}: gradient error ratio {ratio:.3f}"
+    sc = pu.f32_scale(1.0 / math.sqrt(128))
+    refs = oracle.attention_bwd_ref(pu.to_f64(q), pu.to_f64(k), pu.to_f64(v), pu.to_f64(do), causal=causal, scale=sc)
+    bounds = gb.attention_bwd_bound(q, k, v, do, o, lse, refs[1], refs[2], causal=causal, scale=sc,
+                                    dtype=torch.bfloat16)
+    assert_within_bound((dq, dk, dv), refs, bounds, f"MQA 32:1 causal={causal}")
 
 
 @pytest.mark.parametrize("jump", [6.0, 12.5, 13.8, 15.5, 40.0])

@@ -1,6 +1,6 @@
 """GPU parity of the packed variable-length backward (fa_bwd_varlen) against the float64 backward
-oracle: every gradient element, with the tolerance of the dense backward measured per sequence and
-head (each sequence is its own attention problem, so its gradient magnitude is its own). The tokens
+oracle: every gradient element within the elementwise error bound of the dense backward
+(tests/grad_bound.py), formed per sequence (each sequence is its own attention problem). The tokens
 of a sequence without queries get dK = dV = 0 exactly, those of a sequence without keys dQ = 0; one
 packed sequence must reproduce the dense backward bitwise."""
 from __future__ import annotations
@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from tests.parity_util import f32_scale, to_f64
-from tests.test_bwd_parity import _grad_ratio
+from tests import grad_bound as gb
 from tests.test_varlen_parity import _packed
 
 pytestmark = pytest.mark.gpu
@@ -22,11 +22,6 @@ DEV = "cuda:0"
 def _fa():
     import scaled_dot_product_fa2_amd as fa
     return fa
-
-
-def _heads(x: np.ndarray) -> np.ndarray:
-    """(tokens, H, D) -> (1, H, tokens, D), the layout the per-head tolerance is measured on."""
-    return x.transpose(1, 0, 2)[None]
 
 
 def _check(lens_q, lens_k, Hq, Hkv, D, dtype, causal, seed):
@@ -48,6 +43,8 @@ def _check(lens_q, lens_k, Hq, Hkv, D, dtype, causal, seed):
     for name, t in (("dq", gq), ("dk", gk), ("dv", gv)):
         assert np.all(np.isfinite(t)), f"non-finite {name}"
     cqn, ckn = cq.numpy(), ck.numpy()
+    bq, bk, bv = gb.varlen_bwd_bound(q, k, v, do, o, lse, cqn, ckn, rk, rv, causal=causal,
+                                     scale=f32_scale(1.0 / np.sqrt(D)), dtype=dtype)
     worst = 0.0
     for b in range(len(lens_q)):
         q0, q1, k0, k1 = int(cqn[b]), int(cqn[b + 1]), int(ckn[b]), int(ckn[b + 1])
@@ -55,12 +52,12 @@ def _check(lens_q, lens_k, Hq, Hkv, D, dtype, causal, seed):
             # no attention in this sequence: its gradients are exactly zero
             assert np.all(gq[q0:q1] == 0) and np.all(gk[k0:k1] == 0) and np.all(gv[k0:k1] == 0), f"sequence {b}"
             continue
-        floor = 1e-3 * float(np.sqrt(np.mean(to_f64(do[q0:q1]) ** 2)))
-        for name, got, ref in (("dq", gq[q0:q1], rq[q0:q1]), ("dk", gk[k0:k1], rk[k0:k1]),
-                               ("dv", gv[k0:k1], rv[k0:k1])):
-            r = _grad_ratio(_heads(got), _heads(ref), dtype, floor=floor)
-            assert r <= 1.0, f"sequence {b} ({q1 - q0} x {k1 - k0}) {name}: error ratio {r:.3f}"
+        for name, got, ref, bnd in (("dq", gq[q0:q1], rq[q0:q1], bq[q0:q1]), ("dk", gk[k0:k1], rk[k0:k1], bk[k0:k1]),
+                                    ("dv", gv[k0:k1], rv[k0:k1], bv[k0:k1])):
+            r = gb.bound_ratio(got, ref, bnd)
+            assert r <= 1.0, f"sequence {b} ({q1 - q0} x {k1 - k0}) {name}: error / bound {r:.3f}"
             worst = max(worst, r)
+    print(f"[result] varlen bwd: worst gradient error / bound {worst:.4f}", flush=True)
     return worst
 
 
