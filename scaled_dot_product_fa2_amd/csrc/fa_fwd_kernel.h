@@ -222,9 +222,9 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   // ---- persistent loop over this workgroup's items (batch, query head, query tile); see Schedule
   const Schedule sched{p.B * p.Hkv, p.Hkv, p.group, p.n_qtiles, CAUSAL, (int)gridDim.x};
   const int xcd = blockIdx.x % 8;
-  const int64_t n_mine = sched.items_of(xcd);
-  for (int64_t round = 0;; ++round) {
-    const int64_t idx = sched.item_index(blockIdx.x, round);
+  const uint32_t n_mine = sched.items_of(xcd);
+  for (uint32_t round = 0;; ++round) {
+    const uint32_t idx = sched.item_index(blockIdx.x, round);
     if (idx >= n_mine) break;
     const Item item = sched.item(xcd, idx);
     const int b = item.b, h = item.h, qt = item.qt;

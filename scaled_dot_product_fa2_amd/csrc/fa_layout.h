@@ -232,6 +232,9 @@ struct Item {
 };
 
 struct Schedule {
+  // All counts are 32-bit: the host keeps the number of items below 2^31, so every item index,
+  // and an index one round of workgroups past the last item, fits (32-bit division is several
+  // times cheaper than 64-bit on the GPU, and the decode runs before each item's first load).
   int n_units;  // B * Hkv
   int hkv;      // Hkv
   int group;    // Hq / Hkv
@@ -239,46 +242,46 @@ struct Schedule {
   bool causal;
   int grid;     // workgroups launched
 
-  FA_HD int whole() const { return n_units / 8; }  // whole units per XCD
-  FA_HD int rest() const { return n_units % 8; }   // leftover units
-  FA_HD int64_t per_unit() const { return (int64_t)group * n_qt; }
-  FA_HD int64_t n_items() const { return (int64_t)n_units * per_unit(); }
-  FA_HD int64_t n_whole_of() const { return (int64_t)whole() * per_unit(); }  // whole-unit items per XCD
+  typedef uint32_t u32;
+  FA_HD u32 whole() const { return (u32)n_units / 8; }  // whole units per XCD
+  FA_HD u32 rest() const { return (u32)n_units % 8; }   // leftover units
+  FA_HD u32 per_unit() const { return (u32)group * (u32)n_qt; }
+  FA_HD u32 n_items() const { return (u32)n_units * per_unit(); }
+  FA_HD u32 n_whole_of() const { return whole() * per_unit(); }  // whole-unit items per XCD
   // leftover units with their own XCD share (R divides 8), and the share
   FA_HD bool shared_rest() const { return rest() == 1 || rest() == 2 || rest() == 4; }
-  FA_HD int share() const { return rest() > 0 ? 8 / rest() : 8; }
+  FA_HD u32 share() const { return rest() > 0 ? 8 / rest() : 8; }
 
   // The leftover entries of XCD x are taken from a leftover list (one unit's items when the
   // leftover units have their own shares, else all leftover items) in a snake over its m XCDs:
   // sweep k of m consecutive entries goes to XCDs 0 .. m-1 for even k and m-1 .. 0 for odd k, so no
   // XCD always receives the longer item of a sweep. The entries of XCD-in-share a are therefore
   // 2m*k + a and 2m*k + 2m-1-a (k = 0, 1, ...). m is 8 / R (shared) or 8, a power of two.
-  FA_HD int lo_shift() const { return !shared_rest() ? 3 : rest() == 1 ? 3 : rest() == 2 ? 2 : 1; }
-  FA_HD int lo_a(int x) const { return shared_rest() ? x % share() : x; }
-  FA_HD int64_t lo_len() const { return shared_rest() ? per_unit() : (int64_t)rest() * per_unit(); }
+  FA_HD u32 lo_shift() const { return !shared_rest() ? 3 : rest() == 1 ? 3 : rest() == 2 ? 2 : 1; }
+  FA_HD u32 lo_a(int x) const { return shared_rest() ? (u32)x % share() : (u32)x; }
+  FA_HD u32 lo_len() const { return shared_rest() ? per_unit() : rest() * per_unit(); }
   // entries e < n of XCD x's sequence
-  FA_HD int64_t lo_count_below(int x, int64_t n) const {
-    const int a = lo_a(x), period = 2 << lo_shift();
-    const int64_t q = n >> (lo_shift() + 1);
-    const int r = (int)(n & (period - 1));
+  FA_HD u32 lo_count_below(int x, u32 n) const {
+    const u32 a = lo_a(x), period = 2u << lo_shift();
+    const u32 q = n >> (lo_shift() + 1), r = n & (period - 1);
     return 2 * q + (r > a ? 1 : 0) + (r > period - 1 - a ? 1 : 0);
   }
   // entry number k of XCD x's sequence
-  FA_HD int64_t lo_entry(int x, int64_t k) const {
-    const int a = lo_a(x), period = 2 << lo_shift();
+  FA_HD u32 lo_entry(int x, u32 k) const {
+    const u32 a = lo_a(x), period = 2u << lo_shift();
     return (k >> 1) * period + ((k & 1) ? period - 1 - a : a);
   }
   // leftover items of XCD x
-  FA_HD int64_t left_of(int x) const {
+  FA_HD u32 left_of(int x) const {
     if (rest() == 0) return 0;
     if (!causal && !shared_rest()) {  // a contiguous run
-      const int64_t L = lo_len();
-      return L > x ? (L - x + 7) / 8 : 0;
+      const u32 L = lo_len();
+      return L > (u32)x ? (L - (u32)x + 7) / 8 : 0;
     }
     return lo_count_below(x, lo_len());
   }
   // number of items of XCD x
-  FA_HD int64_t items_of(int x) const { return n_whole_of() + left_of(x); }
+  FA_HD u32 items_of(int x) const { return n_whole_of() + left_of(x); }
   // one more than the highest XCD that receives items (the grid must reach it)
   FA_HD int xcds_used() const {
     for (int x = 7; x > 0; --x)
@@ -290,74 +293,74 @@ struct Schedule {
   // grid for at most `max_grid` workgroups: no more than there are items, but at least one
   // workgroup on every XCD that has items
   FA_HD int choose_grid(int64_t max_grid) const {
-    int64_t g = max_grid < n_items() ? max_grid : n_items();
+    int64_t g = max_grid < (int64_t)n_items() ? max_grid : (int64_t)n_items();
     if (g < xcds_used()) g = xcds_used();
     return (int)g;
   }
   // does XCD x hold no more items than workgroups, so that all of them run at once?
-  FA_HD bool one_round(int x) const { return items_of(x) <= wgs_of(x); }
+  FA_HD bool one_round(int x) const { return items_of(x) <= (u32)wgs_of(x); }
 
-  FA_HD Item make(int unit, int g, int t) const {
+  FA_HD Item make(u32 unit, u32 g, u32 t) const {
     Item it;
-    it.b = unit / hkv;
-    it.h = (unit % hkv) * group + g;
-    it.qt = causal ? n_qt - 1 - t : t;  // t is the rank (longest first) under the causal mask
+    it.b = (int)(unit / (u32)hkv);
+    it.h = (int)((unit % (u32)hkv) * (u32)group + g);
+    it.qt = causal ? n_qt - 1 - (int)t : (int)t;  // t is the rank (longest first) under the causal mask
     return it;
   }
   // entry e of the leftover list of XCD x's sequence
-  FA_HD Item left_item(int x, int64_t e) const {
-    const int base = 8 * whole();
+  FA_HD Item left_item(int x, u32 e) const {
+    const u32 base = 8 * whole();
     if (shared_rest()) {
-      const int unit = base + x / share();
-      return causal ? make(unit, (int)(e % group), (int)(e / group)) : make(unit, (int)(e / n_qt), (int)(e % n_qt));
+      const u32 unit = base + (u32)x / share();
+      return causal ? make(unit, e % (u32)group, e / (u32)group) : make(unit, e / (u32)n_qt, e % (u32)n_qt);
     }
     if (causal) {
-      const int64_t per_rank = (int64_t)rest() * group;
-      const int64_t r = e % per_rank;
-      return make(base + (int)(r / group), (int)(r % group), (int)(e / per_rank));
+      const u32 per_rank = rest() * (u32)group;
+      const u32 r = e % per_rank;
+      return make(base + r / (u32)group, r % (u32)group, e / per_rank);
     }
-    const int64_t r = e % per_unit();
-    return make(base + (int)(e / per_unit()), (int)(r / n_qt), (int)(r % n_qt));
+    const u32 r = e % per_unit();
+    return make(base + e / per_unit(), r / (u32)n_qt, r % (u32)n_qt);
   }
   // whole-unit item i of XCD x (0 <= i < n_whole_of()), unit by unit
-  FA_HD Item whole_item(int x, int64_t i) const {
-    const int m = (int)(i / per_unit());
-    const int64_t r = i % per_unit();
-    return causal ? make(x + 8 * m, (int)(r % group), (int)(r / group)) : make(x + 8 * m, (int)(r / n_qt), (int)(r % n_qt));
+  FA_HD Item whole_item(int x, u32 i) const {
+    const u32 m = i / per_unit(), r = i % per_unit();
+    const u32 unit = (u32)x + 8 * m;
+    return causal ? make(unit, r % (u32)group, r / (u32)group) : make(unit, r / (u32)n_qt, r % (u32)n_qt);
   }
   // causal: items of XCD x whose rank is below t (the whole units' and the leftover ones)
-  FA_HD int64_t rank_prefix(int x, int t) const {
-    const int64_t per_rank = shared_rest() ? group : (int64_t)rest() * group;
-    return (int64_t)t * whole() * group + (rest() ? lo_count_below(x, (int64_t)t * per_rank) : 0);
+  FA_HD u32 rank_prefix(int x, u32 t) const {
+    const u32 per_rank = shared_rest() ? (u32)group : rest() * (u32)group;
+    return t * whole() * (u32)group + (rest() ? lo_count_below(x, t * per_rank) : 0);
   }
   // item number i of XCD x (0 <= i < items_of(x))
-  FA_HD Item item(int x, int64_t i) const {
-    const int64_t nw = n_whole_of();
+  FA_HD Item item(int x, u32 i) const {
+    const u32 nw = n_whole_of();
     if (!causal) {
       if (i < nw) return whole_item(x, i);
-      const int64_t k = i - nw;
+      const u32 k = i - nw;
       if (shared_rest()) return left_item(x, lo_entry(x, k));
-      const int64_t L = lo_len();
-      return left_item(x, x * (L / 8) + (x < L % 8 ? x : L % 8) + k);  // x's contiguous run
+      const u32 L = lo_len();
+      return left_item(x, (u32)x * (L / 8) + ((u32)x < L % 8 ? (u32)x : L % 8) + k);  // x's contiguous run
     }
     if (one_round(x)) {
       // longest first over all of the XCD's items: the rank is the largest t with rank_prefix <= i
-      int lo = 0, hi = n_qt - 1;
+      u32 lo = 0, hi = (u32)n_qt - 1;
       while (lo < hi) {
-        const int mid = lo + (hi - lo + 1) / 2;
+        const u32 mid = lo + (hi - lo + 1) / 2;
         if (rank_prefix(x, mid) <= i)
           lo = mid;
         else
           hi = mid - 1;
       }
-      const int64_t off = i - rank_prefix(x, lo);
-      const int64_t wg = (int64_t)whole() * group;
-      if (off < wg) return make(x + 8 * (int)(off / group), (int)(off % group), lo);
-      const int64_t per_rank = shared_rest() ? group : (int64_t)rest() * group;
-      const int64_t k = lo_count_below(x, (int64_t)lo * per_rank) + (off - wg);
+      const u32 off = i - rank_prefix(x, lo);
+      const u32 wg = whole() * (u32)group;
+      if (off < wg) return make((u32)x + 8 * (off / (u32)group), off % (u32)group, lo);
+      const u32 per_rank = shared_rest() ? (u32)group : rest() * (u32)group;
+      const u32 k = lo_count_below(x, lo * per_rank) + (off - wg);
       return left_item(x, lo_entry(x, k));
     }
-    const int64_t nl = left_of(x);
+    const u32 nl = left_of(x);
     if (i < nl) return left_item(x, lo_entry(x, i));
     return whole_item(x, i - nl);
   }
@@ -368,11 +371,12 @@ struct Schedule {
     const int s = k / kCUsPerXCD, c = k % kCUsPerXCD;
     return s * kCUsPerXCD + ((s & 1) ? kCUsPerXCD - 1 - c : c);
   }
-  // index into the XCD's item list of workgroup `wg` in round r (may be >= items_of)
-  FA_HD int64_t item_index(int wg, int64_t r) const {
+  // index into the XCD's item list of workgroup `wg` in round r (may be >= items_of, by less than
+  // one round of workgroups)
+  FA_HD u32 item_index(int wg, u32 r) const {
     const int x = wg % 8, k = wg / 8, gx = wgs_of(x);
     const int pos = cu_snake(k, gx);
-    return r * gx + ((r & 1) ? (gx - 1 - pos) : pos);
+    return r * (u32)gx + (u32)((r & 1) ? (gx - 1 - pos) : pos);
   }
 };
 
