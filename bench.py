@@ -13,9 +13,9 @@ Prints ONE JSON line. Extra objects:
   roofline      - the dominant launch (the non-causal forward): algorithmic FLOP / its average
                   duration from HIP events on the launch stream, against the dense bf16 MFMA peak;
                   `traffic` is the HBM bytes per launch and `sclk_mhz` the shader clock during the
-                  kernel (with `frac_clock_adjusted`, the fraction of the peak at that clock), both
-                  from committed rocprofv3 counters when they were taken on the current kernel
-                  sources, else null.
+                  kernel (with `frac_clock_adjusted`, the fraction of the peak at that clock, null
+                  when the counter reads above the 2.4 GHz maximum), both from committed rocprofv3
+                  counters when they were taken on the current kernel sources, else null.
   workloads     - every named workload (the tiny one, the benchmark shape, the strided D=64 one, the
                   peaked D=256 one and the long GQA one), per mask: time per launch from HIP events,
                   TFLOP/s, fraction of the peak, algorithmic TB/s (Q, K, V read once, O and LSE written
@@ -55,6 +55,19 @@ def kernel_sha() -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+# the shader clock the published peak is quoted at
+PEAK_CLOCK_MHZ = 2400.0
+
+
+def clock_adjusted(frac: float, sclk) -> "float | None":
+    """The fraction of the peak at the clock the kernel ran at, or None without a usable clock. A
+    counter reading above the maximum clock (short launches: the counter also runs while the launch
+    ramps up) bounds nothing and is not used."""
+    if not sclk or sclk > PEAK_CLOCK_MHZ:
+        return None
+    return round(frac * PEAK_CLOCK_MHZ / sclk, 4)
 
 
 def flop(w, causal: bool) -> float:
@@ -186,7 +199,7 @@ def workload_timing(name, stream, min_ms=40.0):
                      "frac_of_peak": round(tf / peak, 4),
                      "algorithmic_tb_per_s": round(algorithmic_bytes(w) / (ms / 1e3) / 1e12, 3),
                      "sclk_mhz": sclk,
-                     "frac_clock_adjusted": round(tf / (peak * sclk / 2400.0), 4) if sclk else None}
+                     "frac_clock_adjusted": clock_adjusted(tf / peak, sclk)}
     del q, k, v, o, lse
     return res
 
@@ -340,7 +353,7 @@ def main():
                 # the published peak is quoted at 2.4 GHz; the clock the kernel actually runs at comes
                 # from the committed GRBM_GUI_ACTIVE counters (profiles/)
                 "sclk_mhz": sclk,
-                "frac_clock_adjusted": round(achieved / (peak * sclk / 2400.0), 4) if sclk else None,
+                "frac_clock_adjusted": clock_adjusted(achieved / peak, sclk),
                 "kernel": f"fa_fwd_kernel<{w.dtype_name}, causal={dominant}, D={w.D}>",
                 "algorithmic_flop_per_launch": flop(w, dominant),
                 "algorithmic_bytes_per_launch": algorithmic_bytes(w)}
