@@ -70,7 +70,8 @@ extern "C" {
  * scale : score scale, a finite float > 0 (typically 1/sqrt(D)).
  * causal: 0 = every key visible; nonzero = top-left causal mask (key j visible to row i iff j <= i).
  * dtype : FA_DTYPE_F16 or FA_DTYPE_BF16, the element type of q, k, v and o.
- * stream: a hipStream_t (NULL = the default stream).
+ * stream: a hipStream_t of the device that holds the buffers (NULL = the default stream of the
+ *         current device, which must then hold them).
  *
  * Sizes: 1 <= B, Hq, Hkv, Nq, Nkv < 2^31; D in {16, 32, 64, 128, 256}; Hq % Hkv == 0.
  * Nq and Nkv need not be multiples of any tile size, and Nq may differ from Nkv.

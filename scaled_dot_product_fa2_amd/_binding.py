@@ -123,6 +123,16 @@ def _stream_for(dev: torch.device, stream):
     return stream
 
 
+def _call_on(dev: torch.device, fn, *args) -> int:
+    """Call a library entry point with `dev` as the current device. A launch on a null stream handle
+    (the default stream) goes to the current device, and fa_bwd_noalloc looks up its array there, so
+    it must be the device the tensors live on."""
+    if torch.cuda.current_device() == dev.index:
+        return fn(*args)
+    with torch.cuda.device(dev):
+        return fn(*args)
+
+
 class FaCall:
     """A validated, pre-marshalled fa_fwd call on fixed tensors: calling it enqueues one forward.
 
@@ -130,13 +140,14 @@ class FaCall:
     only the foreign call. The tensors must stay alive and keep their storage while it is used.
     """
 
-    def __init__(self, args, keepalive):
+    def __init__(self, dev, args, keepalive):
         self._fn = load_library().fa_fwd
+        self._dev = dev
         self._args = args
         self._keepalive = keepalive
 
     def __call__(self) -> None:
-        code = self._fn(*self._args)
+        code = _call_on(self._dev, self._fn, *self._args)
         if code != 0:
             raise FaError(code, fa_strerror(code))
 
@@ -156,20 +167,21 @@ def fa_fwd_call(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
             ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
             B, Hq, Hkv, Nq, Nkv, D, *strides, ctypes.c_float(scale), int(bool(causal)), _DTYPES[q.dtype],
             ctypes.c_void_p(stream.cuda_stream))
-    return FaCall(args, (q, k, v, out, lse, strides))
+    return FaCall(q.device, args, (q, k, v, out, lse, strides))
 
 
 class FaBwdCall:
     """A validated, pre-marshalled fa_bwd call on fixed tensors: calling it enqueues one backward
     (its three kernels). Built by ``fa_bwd_call``; the tensors must stay alive while it is used."""
 
-    def __init__(self, args, keepalive):
+    def __init__(self, dev, args, keepalive):
         self._fn = load_library().fa_bwd
+        self._dev = dev
         self._args = args
         self._keepalive = keepalive
 
     def __call__(self) -> None:
-        code = self._fn(*self._args)
+        code = _call_on(self._dev, self._fn, *self._args)
         if code != 0:
             raise FaError(code, fa_strerror(code))
 
@@ -190,7 +202,7 @@ def fa_bwd_call(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
     ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o, lse, dout, dq, dk, dv, delta)]
     args = (*ptrs, B, Hq, Hkv, Nq, Nkv, D, *strides, ctypes.c_float(scale), int(bool(causal)), _DTYPES[q.dtype],
             ctypes.c_void_p(stream.cuda_stream))
-    return FaBwdCall(args, (q, k, v, o, lse, dout, dq, dk, dv, delta, strides))
+    return FaBwdCall(q.device, args, (q, k, v, o, lse, dout, dq, dk, dv, delta, strides))
 
 
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
@@ -227,8 +239,8 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = 
         raise ValueError("lse must be a contiguous float32 (B, Hq, Nq) tensor")
     _on_device(q.device, out=out, lse=lse)
     stream = _stream_for(q.device, stream)
-    code = load_library().fa_fwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+    code = _call_on(
+        q.device, load_library().fa_fwd, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
         B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(out),
         float(scale), int(bool(causal)), _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream))
     _check(code)
@@ -277,12 +289,13 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
               B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(o), _strides(dout),
               _strides(dq), _strides(dk), _strides(dv), float(scale))
     if window is None:
-        code = load_library().fa_bwd(*common, int(bool(causal)), _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream))
+        code = _call_on(q.device, load_library().fa_bwd, *common, int(bool(causal)), _DTYPES[q.dtype],
+                        ctypes.c_void_p(stream.cuda_stream))
     else:
         if causal:
             raise ValueError("pass either causal or window, not both (the causal mask is window (-1, 0))")
-        code = load_library().fa_bwd_window(*common, int(window[0]), int(window[1]), _DTYPES[q.dtype],
-                                            ctypes.c_void_p(stream.cuda_stream))
+        code = _call_on(q.device, load_library().fa_bwd_window, *common, int(window[0]), int(window[1]),
+                        _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return dq, dk, dv
 
@@ -310,8 +323,8 @@ def fa_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     stream = _stream_for(q.device, stream)
-    _check(load_library().fa_bwd_noalloc(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+    _check(_call_on(
+        q.device, load_library().fa_bwd_noalloc, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v),
         _strides(o), _strides(dout), _strides(dq), _strides(dk), _strides(dv), float(scale), int(bool(causal)),
         _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream)))
@@ -345,8 +358,8 @@ def fa_fwd_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, window_l
         raise ValueError("lse must be a contiguous float32 (B, Hq, Nq) tensor")
     _on_device(q.device, out=out, lse=lse)
     stream = _stream_for(q.device, stream)
-    code = load_library().fa_fwd_window(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+    code = _call_on(
+        q.device, load_library().fa_fwd_window, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
         B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(out),
         float(scale), int(window_left), int(window_right), _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream))
     _check(code)
@@ -362,6 +375,8 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
 
     q: (total_q, Hq, D), k, v: (total_k, Hkv, D) token-major GPU tensors; cu_seqlens_q/k: int32 GPU
     tensors of B + 1 offsets. Returns o (total_q, Hq, D) and lse (Hq, total_q) float32.
+    max_seqlen_q/k must be at least every sequence's length (the offsets stay on the GPU and are not
+    checked here): rows of a longer sequence past it are left unwritten.
     """
     if not q.is_cuda:
         raise ValueError("all tensors must be on the GPU")
@@ -370,8 +385,11 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
         raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
-    if not (cu_seqlens_q.is_contiguous() and cu_seqlens_k.is_contiguous()) or cu_seqlens_q.shape != cu_seqlens_k.shape:
+    if (cu_seqlens_q.dim() != 1 or not (cu_seqlens_q.is_contiguous() and cu_seqlens_k.is_contiguous())
+            or cu_seqlens_q.shape != cu_seqlens_k.shape):
         raise ValueError("cu_seqlens_q and cu_seqlens_k must be contiguous with B + 1 entries each")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D token-major (total, H, D) tensors")
     total_q, Hq, D = q.shape
     total_k, Hkv, _ = k.shape
     if k.shape != (total_k, Hkv, D) or v.shape != k.shape:
@@ -393,8 +411,8 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
     def st3(t):
         return (ctypes.c_int64 * 3)(*t.stride())
 
-    code = load_library().fa_fwd_varlen(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
+    code = _call_on(
+        q.device, load_library().fa_fwd_varlen, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
         cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D,
         st3(q), st3(k), st3(v), st3(out), float(scale), int(bool(causal)), _DTYPES[q.dtype],
         ctypes.c_void_p(stream.cuda_stream))
@@ -420,8 +438,11 @@ def fa_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
         raise ValueError("q, k, v, o, dout must share one dtype, float16 or bfloat16")
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
-    if not (cu_seqlens_q.is_contiguous() and cu_seqlens_k.is_contiguous()) or cu_seqlens_q.shape != cu_seqlens_k.shape:
+    if (cu_seqlens_q.dim() != 1 or not (cu_seqlens_q.is_contiguous() and cu_seqlens_k.is_contiguous())
+            or cu_seqlens_q.shape != cu_seqlens_k.shape):
         raise ValueError("cu_seqlens_q and cu_seqlens_k must be contiguous with B + 1 entries each")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D token-major (total, H, D) tensors")
     total_q, Hq, D = q.shape
     total_k, Hkv, _ = k.shape
     if k.shape != (total_k, Hkv, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
@@ -447,8 +468,8 @@ def fa_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     def st3(t):
         return (ctypes.c_int64 * 3)(*t.stride())
 
-    code = load_library().fa_bwd_varlen(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+    code = _call_on(
+        q.device, load_library().fa_bwd_varlen, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
         dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv,
         total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D, st3(q), st3(k), st3(v), st3(o), st3(dout),
         st3(dq), st3(dk), st3(dv), float(scale), int(bool(causal)), _DTYPES[q.dtype],

@@ -85,7 +85,7 @@ int check_strides(const int64_t* st, bool is_output, int64_t B, int64_t H, int64
   if (st[3] != 1) return FA_ERR_LAYOUT;
   for (int i = 0; i < 3; ++i) {
     if (st[i] < 0) return FA_ERR_LAYOUT;
-    if ((st[i] * 2) % 16 != 0) return FA_ERR_LAYOUT;
+    if (st[i] % 8 != 0) return FA_ERR_LAYOUT;  // 16-byte multiples of 2-byte elements
   }
   if (st[2] > kMaxRowStride) return FA_ERR_LAYOUT;
   if (is_output) {
@@ -296,6 +296,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   const int64_t ks[4] = {0, k_stride[1], k_stride[0], k_stride[2]};
   const int64_t vs[4] = {0, v_stride[1], v_stride[0], v_stride[2]};
   const int64_t os[4] = {0, o_stride[1], o_stride[0], o_stride[2]};
+  // every token writes its own output row: the token stride of O is checked against all tokens here
+  // (the per-sequence check below sees only the longest sequence, which may be one token long)
+  if (total_q > 1 && o_stride[0] == 0) return FA_ERR_LAYOUT;
   if (!extent_ok(1, Hq, total_q, D, qs) || !extent_ok(1, Hkv, total_k, D, ks) || !extent_ok(1, Hkv, total_k, D, vs) ||
       !extent_ok(1, Hq, total_q, D, os))
     return FA_ERR_SHAPE;

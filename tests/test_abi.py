@@ -276,6 +276,9 @@ VL_BAD = [
     ("head_dim", dict(D=40), "FA_ERR_HEAD_DIM"), ("gqa", dict(Hq=3), "FA_ERR_GQA"),
     ("dim_stride", dict(qs=(256, 64, 2)), "FA_ERR_LAYOUT"), ("dtype", dict(dtype=9), "FA_ERR_DTYPE"),
     ("extent_overflow", dict(qs=(1 << 55, 64, 1)), "FA_ERR_SHAPE"),
+    ("o_zero_token_stride", dict(os=(0, 64, 1)), "FA_ERR_LAYOUT"),
+    # one-token sequences: the zero token stride would make every sequence write the same O row
+    ("o_zero_token_stride_one_token_seqs", dict(mq=1, os=(0, 64, 1)), "FA_ERR_LAYOUT"),
 ]
 
 
