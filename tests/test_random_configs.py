@@ -1,0 +1,115 @@
+"""Seeded random configurations: every axis of the forward and the backward at once.
+
+The other parity tests vary one axis at a time (head dim, dtype, head group, lengths, mask,
+storage layout, scale). Here each case draws all of them together from a seeded generator, so
+their interactions -- a D = 16 head with a group of three in BSND storage under a sliding window
+with Nq != Nkv, say -- are compared element by element with the float64 oracles too: O and LSE
+within the forward tolerances, dQ, dK and dV within the derived error bound of tests/grad_bound.py.
+The case list is fixed by the seed; each case prints its draw before it runs.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import grad_bound as gb
+from tests.parity_util import LSE_ATOL, O_TOL, f32_scale, o_ratio, to_f64
+from tests.test_bwd_parity import assert_within_bound
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _draw_cases(n: int, seed: int):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 3]))
+        mask = str(rng.choice(["full", "causal", "window"]))
+        cases.append(dict(
+            D=int(rng.choice([16, 32, 64, 128, 256])),
+            dtype=[torch.bfloat16, torch.float16][int(rng.integers(2))],
+            B=int(rng.integers(1, 3)), Hkv=hkv, Hq=hkv * int(rng.choice([1, 2, 3, 4])),
+            Nq=int(rng.integers(1, 330)), Nkv=int(rng.integers(1, 330)),
+            mask=mask,
+            # window sides: -1 is unbounded; a finite side is anything from 0 to beyond the sequence
+            left=int(rng.integers(-1, 200)), right=int(rng.integers(-1, 60)),
+            q_layout=str(rng.choice(["bnsd", "bsnd"])), kv_layout=str(rng.choice(["bnsd", "bsnd"])),
+            scale=None if rng.random() < 0.5 else float(rng.uniform(0.03, 0.4)),
+            q_mult=float(rng.choice([1.0, 1.0, 4.0])),
+            seed=seed * 1000 + i))
+    return cases
+
+
+FWD = _draw_cases(32, 17)
+BWD = _draw_cases(16, 29)
+
+
+def _id(c):
+    dt = "bf16" if c["dtype"] == torch.bfloat16 else "fp16"
+    m = c["mask"] if c["mask"] != "window" else f"w{c['left']}_{c['right']}"
+    return f"d{c['D']}-{dt}-b{c['B']}h{c['Hq']}kv{c['Hkv']}-{c['Nq']}x{c['Nkv']}-{m}-{c['q_layout']}{c['kv_layout']}"
+
+
+def _inputs(c):
+    q, k, v = workloads.make_random(c["B"], c["Hq"], c["Hkv"], c["Nq"], c["Nkv"], c["D"], c["dtype"], seed=c["seed"],
+                                    q_mult=c["q_mult"], kv_layout=c["kv_layout"], q_layout=c["q_layout"])
+    return q, k, v
+
+
+def _window(c):
+    if c["mask"] != "window":
+        return None
+    return (None if c["left"] < 0 else c["left"], None if c["right"] < 0 else c["right"])
+
+
+def _forward(fa, c, qd, kd, vd):
+    if c["mask"] == "window":
+        return fa.fa_fwd_window(qd, kd, vd, window_left=c["left"], window_right=c["right"], scale=c["scale"])
+    return fa.fa_fwd(qd, kd, vd, causal=c["mask"] == "causal", scale=c["scale"])
+
+
+@pytest.mark.parametrize("c", FWD, ids=[_id(c) for c in FWD])
+def test_random_forward(c):
+    import scaled_dot_product_fa2_amd as fa
+    print(f"[case] forward {_id(c)} scale={c['scale']} q_mult={c['q_mult']} seed={c['seed']}", flush=True)
+    q, k, v = _inputs(c)
+    o, lse = _forward(fa, c, q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    s = f32_scale(c["scale"] if c["scale"] is not None else 1.0 / np.sqrt(c["D"]))
+    o_ref, l_ref = oracle.attention_ref(to_f64(q), to_f64(k), to_f64(v), causal=c["mask"] == "causal", scale=s,
+                                        window=_window(c))
+    og, lg = to_f64(o), to_f64(lse)
+    assert np.all(np.isfinite(og)), "non-finite O"
+    ratio = o_ratio(og, o_ref, c["dtype"])
+    empty = np.isneginf(l_ref)  # rows whose window holds no key: O = 0, LSE = -inf
+    assert np.array_equal(np.isneginf(lg), empty), "LSE = -inf exactly on the rows without keys"
+    lerr = float(np.max(np.abs(lg[~empty] - l_ref[~empty]))) if (~empty).any() else 0.0
+    print(f"[result] forward {_id(c)}: O error ratio {ratio:.3f}, LSE error {lerr:.2e}", flush=True)
+    assert ratio <= 1.0, f"O error ratio {ratio:.3f} > 1 ({O_TOL[c['dtype']]})"
+    assert lerr <= LSE_ATOL, f"LSE error {lerr:.2e}"
+
+
+@pytest.mark.parametrize("c", BWD, ids=[_id(c) for c in BWD])
+def test_random_backward(c):
+    import scaled_dot_product_fa2_amd as fa
+    print(f"[case] backward {_id(c)} scale={c['scale']} q_mult={c['q_mult']} seed={c['seed']}", flush=True)
+    q, k, v = _inputs(c)
+    g = torch.Generator().manual_seed(c["seed"] + 1)
+    do = torch.randn(c["B"], c["Hq"], c["Nq"], c["D"], generator=g).to(c["dtype"])
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse = _forward(fa, c, qd, kd, vd)
+    win = None if c["mask"] != "window" else (c["left"], c["right"])
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, lse, dod, causal=c["mask"] == "causal", scale=c["scale"], window=win)
+    torch.cuda.synchronize()
+    s = f32_scale(c["scale"] if c["scale"] is not None else 1.0 / np.sqrt(c["D"]))
+    causal = c["mask"] == "causal"
+    refs = oracle.attention_bwd_ref(to_f64(q), to_f64(k), to_f64(v), to_f64(do), causal=causal, scale=s,
+                                    window=_window(c))
+    bounds = gb.attention_bwd_bound(q, k, v, do, o, lse, refs[1], refs[2], causal=causal, scale=s, dtype=c["dtype"],
+                                    window=_window(c))
+    assert_within_bound((dq, dk, dv), refs, bounds, f"backward {_id(c)}")
