@@ -14,8 +14,8 @@ Prints ONE JSON line. Extra objects:
                   duration from HIP events on the launch stream, against the dense bf16 MFMA peak;
                   `traffic` is the HBM bytes per launch and `sclk_mhz` the shader clock during the
                   kernel (with `frac_clock_adjusted`, the fraction of the peak at that clock, null
-                  when the counter reads above the 2.4 GHz maximum), both from committed rocprofv3
-                  counters when they were taken on the current kernel sources, else null.
+                  for launches under 0.1 ms, where the counter reads high), both from committed
+                  rocprofv3 counters when they were taken on the current kernel sources, else null.
   workloads     - every named workload (the tiny one, the benchmark shape, the strided D=64 one, the
                   peaked D=256 one and the long GQA one), per mask: time per launch from HIP events,
                   TFLOP/s, fraction of the peak, algorithmic TB/s (Q, K, V read once, O and LSE written
@@ -61,11 +61,17 @@ def kernel_sha() -> str:
 PEAK_CLOCK_MHZ = 2400.0
 
 
-def clock_adjusted(frac: float, sclk) -> "float | None":
-    """The fraction of the peak at the clock the kernel ran at, or None without a usable clock. A
-    counter reading above the maximum clock (short launches: the counter also runs while the launch
-    ramps up) bounds nothing and is not used."""
-    if not sclk or sclk > PEAK_CLOCK_MHZ:
+# launches shorter than this read a clock from the counters that is too high to use (below)
+CLOCK_MIN_LAUNCH_MS = 0.1
+
+
+def clock_adjusted(frac: float, sclk, launch_ms: float) -> "float | None":
+    """The fraction of the peak at the clock the kernel ran at, or None without a usable clock.
+    GRBM_GUI_ACTIVE over a dispatch also counts while the launch ramps up and drains, so on launches
+    of a few tens of microseconds it reads far above the shader clock the waves see (2.4 GHz and
+    more where timestamps taken inside the kernel give about 1.7 GHz); it is used only on longer
+    launches and never above the maximum clock."""
+    if not sclk or sclk > PEAK_CLOCK_MHZ or launch_ms < CLOCK_MIN_LAUNCH_MS:
         return None
     return round(frac * PEAK_CLOCK_MHZ / sclk, 4)
 
@@ -199,7 +205,7 @@ def workload_timing(name, stream, min_ms=40.0):
                      "frac_of_peak": round(tf / peak, 4),
                      "algorithmic_tb_per_s": round(algorithmic_bytes(w) / (ms / 1e3) / 1e12, 3),
                      "sclk_mhz": sclk,
-                     "frac_clock_adjusted": clock_adjusted(tf / peak, sclk)}
+                     "frac_clock_adjusted": clock_adjusted(tf / peak, sclk, ms)}
     del q, k, v, o, lse
     return res
 
@@ -353,7 +359,7 @@ def main():
                 # the published peak is quoted at 2.4 GHz; the clock the kernel actually runs at comes
                 # from the committed GRBM_GUI_ACTIVE counters (profiles/)
                 "sclk_mhz": sclk,
-                "frac_clock_adjusted": clock_adjusted(achieved / peak, sclk),
+                "frac_clock_adjusted": clock_adjusted(achieved / peak, sclk, dom_ms),
                 "kernel": f"fa_fwd_kernel<{w.dtype_name}, causal={dominant}, D={w.D}>",
                 "algorithmic_flop_per_launch": flop(w, dominant),
                 "algorithmic_bytes_per_launch": algorithmic_bytes(w)}
