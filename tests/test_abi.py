@@ -319,3 +319,34 @@ VLB_BAD = [
 @pytest.mark.parametrize("name,over,code", VLB_BAD, ids=[b[0] for b in VLB_BAD])
 def test_varlen_bwd_validation_rejects(name, over, code):
     assert _vlb_call(**over) == D_[code]
+
+
+def test_launch_runs_with_the_tensors_device_current(monkeypatch):
+    """A launch on a null stream handle goes to the current device, so the binding makes the tensors'
+    device current around each library call, and only when another device is current (host logic,
+    with the device calls replaced by stand-ins)."""
+    import torch
+    from scaled_dot_product_fa2_amd import _binding
+    state = {"current": 0, "entered": []}
+
+    class _Guard:
+        def __init__(self, dev):
+            self.dev = dev
+
+        def __enter__(self):
+            state["entered"].append(self.dev.index)
+            self.prev, state["current"] = state["current"], self.dev.index
+
+        def __exit__(self, *exc):
+            state["current"] = self.prev
+            return False
+
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: state["current"])
+    monkeypatch.setattr(torch.cuda, "device", _Guard)
+    seen = []
+    fn = lambda *args: seen.append((state["current"], args)) or 0
+    assert _binding._call_on(torch.device("cuda", 0), fn, 1, 2) == 0
+    assert seen[-1] == (0, (1, 2)) and state["entered"] == []      # already current: no switch
+    assert _binding._call_on(torch.device("cuda", 3), fn, 7) == 0
+    assert seen[-1] == (3, (7,)) and state["entered"] == [3]       # switched for the call
+    assert state["current"] == 0                                   # and back afterwards
