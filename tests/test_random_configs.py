@@ -5,6 +5,8 @@ storage layout, scale). Here each case draws all of them together from a seeded 
 their interactions -- a D = 16 head with a group of three in BSND storage under a sliding window
 with Nq != Nkv, say -- are compared element by element with the float64 oracles too: O and LSE
 within the forward tolerances, dQ, dK and dV within the derived error bound of tests/grad_bound.py.
+Packed variable-length sequences are drawn the same way (sequence count, query and key lengths with
+empty sequences among them, head dim, dtype, group, mask) and go through the varlen entry points.
 The case list is fixed by the seed; each case prints its draw before it runs.
 """
 from __future__ import annotations
@@ -113,3 +115,46 @@ def test_random_backward(c):
     bounds = gb.attention_bwd_bound(q, k, v, do, o, lse, refs[1], refs[2], causal=causal, scale=s, dtype=c["dtype"],
                                     window=_window(c))
     assert_within_bound((dq, dk, dv), refs, bounds, f"backward {_id(c)}")
+
+
+# Packed variable-length sequences: a random number of sequences with random query and key lengths
+# (empty ones included), head dim, dtype, head group and mask, through the varlen entry points.
+def _draw_varlen(n: int, seed: int):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        nseq = int(rng.integers(1, 7))
+        lens_q = [int(x) if rng.random() > 0.12 else 0 for x in rng.integers(1, 300, nseq)]
+        lens_k = [int(x) if rng.random() > 0.12 else 0 for x in rng.integers(1, 300, nseq)]
+        if sum(lens_q) == 0:
+            lens_q[0] = int(rng.integers(1, 100))
+        if sum(lens_k) == 0:
+            lens_k[-1] = int(rng.integers(1, 100))
+        hkv = int(rng.choice([1, 2]))
+        cases.append(dict(lens_q=lens_q, lens_k=lens_k, Hkv=hkv, Hq=hkv * int(rng.choice([1, 2, 4])),
+                          D=int(rng.choice([16, 32, 64, 128, 256])),
+                          dtype=[torch.bfloat16, torch.float16][int(rng.integers(2))],
+                          causal=bool(rng.integers(2)), seed=seed * 1000 + i))
+    return cases
+
+
+VL_FWD = _draw_varlen(16, 41)
+VL_BWD = _draw_varlen(8, 43)
+
+
+def _vl_id(c):
+    dt = "bf16" if c["dtype"] == torch.bfloat16 else "fp16"
+    return f"d{c['D']}-{dt}-h{c['Hq']}kv{c['Hkv']}-{len(c['lens_q'])}seq-{'causal' if c['causal'] else 'full'}"
+
+
+@pytest.mark.parametrize("c", VL_FWD, ids=[_vl_id(c) for c in VL_FWD])
+def test_random_varlen_forward(c):
+    from tests import test_varlen_parity as vp
+    r = vp._check(c["lens_q"], c["lens_k"], c["Hq"], c["Hkv"], c["D"], c["dtype"], c["causal"], c["seed"])
+    print(f"[result] varlen forward {_vl_id(c)}: O error ratio {r:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("c", VL_BWD, ids=[_vl_id(c) for c in VL_BWD])
+def test_random_varlen_backward(c):
+    from tests import test_varlen_bwd_parity as vbp
+    vbp._check(c["lens_q"], c["lens_k"], c["Hq"], c["Hkv"], c["D"], c["dtype"], c["causal"], c["seed"])
