@@ -12,10 +12,10 @@ Prints ONE JSON line. Extra objects:
                   products of the backward (10*B*Hq*Nq*Nkv*D, halved for the causal mask).
   roofline      - the dominant launch (the non-causal forward): algorithmic FLOP / its average
                   duration from HIP events on the launch stream, against the dense bf16 MFMA peak;
-                  `traffic` is the HBM bytes per launch and `sclk_mhz` the shader clock during the
-                  kernel (with `frac_clock_adjusted`, the fraction of the peak at that clock, null
-                  for launches under 0.1 ms, where the counter reads high), both from committed
-                  rocprofv3 counters when they were taken on the current kernel sources, else null.
+                  `traffic` is the HBM bytes per launch from committed rocprofv3 counters and
+                  `sclk_mhz` the shader clock the waves hold (`sclk_source` says from where; with
+                  `frac_clock_adjusted`, the fraction of the peak at that clock), both null unless
+                  taken on the current kernel sources.
   workloads     - every named workload (the tiny one, the benchmark shape, the strided D=64 one, the
                   peaked D=256 one and the long GQA one), per mask: time per launch from HIP events,
                   TFLOP/s, fraction of the peak, algorithmic TB/s (Q, K, V read once, O and LSE written
@@ -26,6 +26,13 @@ Prints ONE JSON line. Extra objects:
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                       [--no-backward] [--no-workloads]
        python bench.py --sweep | --sweep-backward   (throughput over a fixed list of shapes instead)
+       python bench.py --timeline [--workload NAME] [--timeline-warmup-ms MS]  (per-workgroup clock stamps of one forward launch
+                      per mask from libfa_timeline.so, built by `python -m scaled_dot_product_fa2_amd.build
+                      --timeline`: the shader clock the waves hold and where the launch's time goes)
+
+The shader clock behind `frac_clock_adjusted` comes from a committed timeline summary
+(profiles/timeline_<workload>.json) when one matches the kernel sources, else from the
+GRBM_GUI_ACTIVE counter on launches of 0.1 ms or more.
 """
 from __future__ import annotations
 
@@ -61,19 +68,38 @@ def kernel_sha() -> str:
 PEAK_CLOCK_MHZ = 2400.0
 
 
-# launches shorter than this read a clock from the counters that is too high to use (below)
+# GRBM_GUI_ACTIVE over a dispatch also counts while the launch ramps up and drains, so on launches of
+# a few tens of microseconds it reads far above the shader clock the waves see (2.4 GHz where the
+# in-kernel timestamps give about 1.7 GHz); below this launch time it is not used
 CLOCK_MIN_LAUNCH_MS = 0.1
 
 
-def clock_adjusted(frac: float, sclk, launch_ms: float) -> "float | None":
-    """The fraction of the peak at the clock the kernel ran at, or None without a usable clock.
-    GRBM_GUI_ACTIVE over a dispatch also counts while the launch ramps up and drains, so on launches
-    of a few tens of microseconds it reads far above the shader clock the waves see (2.4 GHz and
-    more where timestamps taken inside the kernel give about 1.7 GHz); it is used only on longer
-    launches and never above the maximum clock."""
-    if not sclk or sclk > PEAK_CLOCK_MHZ or launch_ms < CLOCK_MIN_LAUNCH_MS:
+def load_timeline(workload: str, mode: str):
+    """The median in-kernel shader clock (MHz) of a launch from the committed timeline summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"timeline_{workload}.json")
+    if not os.path.exists(path):
         return None
-    return round(frac * PEAK_CLOCK_MHZ / sclk, 4)
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    m = rec.get("modes", {}).get(mode)
+    return None if m is None else m.get("sclk_mhz_median")
+
+
+def held_clock(workload: str, mode: str, launch_ms: float):
+    """(clock MHz, source) for the clock-adjusted fraction: the in-kernel timeline clock when a
+    committed summary matches, else the counter clock where it is usable (CLOCK_MIN_LAUNCH_MS)."""
+    tl = load_timeline(workload, mode)
+    if tl:
+        return tl, "in-kernel timestamps"
+    sclk = load_profile(workload, mode, "sclk_mhz")
+    if sclk and sclk <= PEAK_CLOCK_MHZ and launch_ms >= CLOCK_MIN_LAUNCH_MS:
+        return sclk, "GRBM_GUI_ACTIVE"
+    return None, None
 
 
 def flop(w, causal: bool) -> float:
@@ -200,12 +226,12 @@ def workload_timing(name, stream, min_ms=40.0):
         ms = e0.elapsed_time(e1) / reps
         tf = flop(w, c) / (ms / 1e3) / 1e12
         mode = "causal" if c else "non_causal"
-        sclk = load_profile(w.name, mode, "sclk_mhz")
+        sclk, src = held_clock(w.name, mode, ms)
         res[mode] = {"ms_per_launch": round(ms, 5), "launches": reps, "tflops": round(tf, 2),
                      "frac_of_peak": round(tf / peak, 4),
                      "algorithmic_tb_per_s": round(algorithmic_bytes(w) / (ms / 1e3) / 1e12, 3),
-                     "sclk_mhz": sclk,
-                     "frac_clock_adjusted": clock_adjusted(tf / peak, sclk, ms)}
+                     "sclk_mhz": sclk, "sclk_source": src,
+                     "frac_clock_adjusted": round(tf / peak * PEAK_CLOCK_MHZ / sclk, 4) if sclk else None}
     del q, k, v, o, lse
     return res
 
@@ -263,6 +289,71 @@ def sweep(backward: bool):
         del q, k, v, do, o, lse
 
 
+TIMELINE_LIB = os.path.join(ROOT, "scaled_dot_product_fa2_amd", "libfa_timeline.so")
+REALTIME_MHZ = 100.0  # s_memrealtime counts a fixed 100 MHz clock
+
+
+def timeline(w, warmup_ms: float) -> None:
+    """--timeline: one forward launch per mask through libfa_timeline.so (the same kernels with
+    per-workgroup clock stamps), after back-to-back launches of the same mask for at least
+    `warmup_ms` (the clock settles over tens of milliseconds of load); prints one JSON line with the
+    shader clock the waves held (s_memtime against s_memrealtime over each workgroup's life) and the
+    phases of each workgroup's first item, as median and range over workgroups."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import workloads
+    import scaled_dot_product_fa2_amd as fa
+    from scaled_dot_product_fa2_amd import _binding
+
+    if not os.path.exists(TIMELINE_LIB):
+        raise SystemExit(f"{TIMELINE_LIB} is missing: build it with "
+                         f"`python -m scaled_dot_product_fa2_amd.build --timeline`")
+    _binding._lib = _binding.load_library(TIMELINE_LIB)  # every call below goes to the stamping build
+    read = getattr(_binding._lib, f"fa_timeline_read_t{1 if w.dtype_name == 'bf16' else 0}_d{w.D}")
+    read.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    read.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    rec = {"workload": w.name, "kernel_sha": kernel_sha(), "warmup_ms": warmup_ms, "modes": {}}
+    for c in w.causal_modes:
+        grid = fa.fa_fwd_plan(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, c, w.dtype)["grid"]
+        o = torch.empty(w.B, w.Hq, w.Nq, w.D, dtype=w.dtype, device=dev)
+        lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=dev)
+        call = fa.fa_fwd_call(q, k, v, o, lse, causal=c)
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < warmup_ms:
+            for _ in range(10):
+                call()
+            torch.cuda.synchronize()
+        call()
+        torch.cuda.synchronize()
+        buf = np.zeros(grid * 8, dtype=np.uint64)
+        if read(buf.ctypes.data, grid * 8) != 0:
+            raise RuntimeError("reading the timeline failed")
+        t = buf.reshape(grid, 8).astype(np.int64)
+        us = (t[:, :4] - t[:, 0].min()) / REALTIME_MHZ
+        life = np.maximum(t[:, 3] - t[:, 0], 1)
+        mhz = (t[:, 7] - t[:, 6]) / life * REALTIME_MHZ
+        loop_clocks = (t[:, 2] - t[:, 1]) / REALTIME_MHZ * mhz
+        tiles = np.maximum(t[:, 5], 1)
+
+        def stat(x):
+            return {"median": round(float(np.median(x)), 2), "min": round(float(np.min(x)), 2),
+                    "max": round(float(np.max(x)), 2)}
+
+        rec["modes"]["causal" if c else "non_causal"] = {
+            "workgroups": grid, "span_us": round(float(us[:, 3].max()), 2),
+            "sclk_mhz_median": round(float(np.median(mhz)), 1), "sclk_mhz": stat(mhz),
+            "start_us": stat(us[:, 0]), "first_item_prologue_us": stat(us[:, 1] - us[:, 0]),
+            "first_item_loop_us": stat(us[:, 2] - us[:, 1]), "end_us": stat(us[:, 3]),
+            "first_item_clocks_per_tile": stat(loop_clocks / tiles),
+            "first_item_wait_share": round(float(np.median(t[:, 4] / np.maximum(loop_clocks, 1))), 4)}
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,6 +367,10 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark: forward TFLOP/s over a fixed list of shapes, one JSON line each")
     ap.add_argument("--sweep-backward", action="store_true", help="the same for the backward (five-product TFLOP/s)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-workgroup clock stamps of one forward launch per mask (libfa_timeline.so)")
+    ap.add_argument("--timeline-warmup-ms", type=float, default=200.0,
+                    help="back-to-back launches before the stamped one, in milliseconds")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB, 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -287,6 +382,10 @@ def main():
     import torch
     import workloads
     import scaled_dot_product_fa2_amd as fa
+
+    if args.timeline:
+        timeline(workloads.WORKLOADS[args.workload], args.timeline_warmup_ms)
+        return
 
     if args.sweep or args.sweep_backward:
         sweep(backward=args.sweep_backward)
@@ -352,14 +451,14 @@ def main():
     dominant = max(modes, key=lambda c: per_mode_ms[c])
     dom_ms = per_mode_ms[dominant] / args.steps
     achieved = flop(w, dominant) / (dom_ms / 1e3) / 1e12
-    sclk = load_profile(w.name, mode_name[dominant], "sclk_mhz")
+    sclk, sclk_src = held_clock(w.name, mode_name[dominant], dom_ms)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),
                 "traffic": load_profile(w.name, mode_name[dominant], "hbm_bytes_per_launch"),
-                # the published peak is quoted at 2.4 GHz; the clock the kernel actually runs at comes
-                # from the committed GRBM_GUI_ACTIVE counters (profiles/)
-                "sclk_mhz": sclk,
-                "frac_clock_adjusted": clock_adjusted(achieved / peak, sclk, dom_ms),
+                # the published peak is quoted at 2.4 GHz; the clock the waves actually hold comes from
+                # a committed timeline or counter summary (profiles/)
+                "sclk_mhz": sclk, "sclk_source": sclk_src,
+                "frac_clock_adjusted": round(achieved / peak * PEAK_CLOCK_MHZ / sclk, 4) if sclk else None,
                 "kernel": f"fa_fwd_kernel<{w.dtype_name}, causal={dominant}, D={w.D}>",
                 "algorithmic_flop_per_launch": flop(w, dominant),
                 "algorithmic_bytes_per_launch": algorithmic_bytes(w)}

@@ -4,7 +4,11 @@ The kernel instances are compiled per (element type, head dim) as separate objec
 (fa_fwd_inst.hip and fa_bwd_inst.hip with -DFA_INST_T / -DFA_INST_D), next to the C ABI in
 fa_api.hip; the objects are then linked into one shared library.
 
-Usage: python -m scaled_dot_product_fa2_amd.build [-j JOBS]
+Usage: python -m scaled_dot_product_fa2_amd.build [-j JOBS] [--timeline]
+
+--timeline builds libfa_timeline.so instead: the same sources compiled with -DFA_TIMELINE, whose
+forward kernels also record per-workgroup clock stamps (bench.py --timeline reads them). libfa.so,
+which the binding loads, never contains them.
 """
 from __future__ import annotations
 
@@ -21,6 +25,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+TIMELINE_LIB_PATH = os.path.join(PKG_DIR, "libfa_timeline.so")
 HEAD_DIMS = (16, 32, 64, 128, 256)
 DTYPES = ((0, "f16"), (1, "bf16"))
 
@@ -32,15 +37,16 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", *DEVICE_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def compile_jobs():
+def compile_jobs(obj_dir: str = OBJ_DIR, extra=()):
     """(object path, hipcc command) for every translation unit."""
-    api = os.path.join(OBJ_DIR, "fa_api.o")
-    jobs = [(api, [HIPCC, *COMMON, "-c", os.path.join(CSRC, "fa_api.hip"), "-o", api])]
+    flags = [*COMMON, *extra]
+    api = os.path.join(obj_dir, "fa_api.o")
+    jobs = [(api, [HIPCC, *flags, "-c", os.path.join(CSRC, "fa_api.hip"), "-o", api])]
     for part in ("bwd", "fwd"):  # the backward instances are the slower ones: start them first
         for d in sorted(HEAD_DIMS, reverse=True):
             for t, tn in DTYPES:
-                obj = os.path.join(OBJ_DIR, f"fa_{part}_{tn}_d{d}.o")
-                jobs.append((obj, [HIPCC, *COMMON, f"-DFA_INST_T={t}", f"-DFA_INST_D={d}", "-c",
+                obj = os.path.join(obj_dir, f"fa_{part}_{tn}_d{d}.o")
+                jobs.append((obj, [HIPCC, *flags, f"-DFA_INST_T={t}", f"-DFA_INST_D={d}", "-c",
                                    os.path.join(CSRC, f"fa_{part}_inst.hip"), "-o", obj]))
     return jobs
 
@@ -52,10 +58,13 @@ def _run(cmd):
     return res.returncode, "\n".join(lines)
 
 
-def build(verbose: bool = True, jobs: int | None = None) -> str:
-    """Compile every instance and the C ABI, link libfa.so in place (atomically replaced)."""
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    todo = compile_jobs()
+def build(verbose: bool = True, jobs: int | None = None, timeline: bool = False) -> str:
+    """Compile every instance and the C ABI, link libfa.so in place (atomically replaced); with
+    timeline=True the clock-stamping variant libfa_timeline.so instead."""
+    obj_dir = os.path.join(OBJ_DIR, "timeline") if timeline else OBJ_DIR
+    lib_path = TIMELINE_LIB_PATH if timeline else LIB_PATH
+    os.makedirs(obj_dir, exist_ok=True)
+    todo = compile_jobs(obj_dir, ("-DFA_TIMELINE",) if timeline else ())
     if jobs is None:
         jobs = min(16, len(os.sched_getaffinity(0)))
     if verbose:
@@ -67,7 +76,7 @@ def build(verbose: bool = True, jobs: int | None = None) -> str:
         for (obj, cmd), out in failed:
             sys.stderr.write(f"[build] FAILED: {' '.join(cmd)}\n{out}\n")
         raise RuntimeError(f"hipcc failed on {len(failed)} translation unit(s)")
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for o, _ in todo], "-o", tmp]
     if verbose:
         print("[build]", " ".join(link), flush=True)
@@ -75,8 +84,8 @@ def build(verbose: bool = True, jobs: int | None = None) -> str:
     if rc != 0:
         sys.stderr.write(out + "\n")
         raise RuntimeError(f"link failed with exit code {rc}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 def clean() -> None:
@@ -86,5 +95,6 @@ def clean() -> None:
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", "--jobs", type=int, default=None)
+    ap.add_argument("--timeline", action="store_true", help="build libfa_timeline.so (clock stamps)")
     args = ap.parse_args()
-    build(jobs=args.jobs)
+    build(jobs=args.jobs, timeline=args.timeline)

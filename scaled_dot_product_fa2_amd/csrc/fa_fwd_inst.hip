@@ -32,3 +32,16 @@ template int launch_fwd<InstT, false, FA_INST_D, false, true>(const FwdParams&, 
 template int launch_fwd<InstT, true, FA_INST_D, false, true>(const FwdParams&, int64_t, hipStream_t);
 
 }  // namespace fa
+
+#ifdef FA_TIMELINE
+// Timeline build only: copy this instance's timeline words (see g_timeline) to host memory.
+#define FA_TL_JOIN(a, b, c, d) a##b##c##d
+#define FA_TL_NAME(t, d) FA_TL_JOIN(fa_timeline_read_t, t, _d, d)
+extern "C" int FA_TL_NAME(FA_INST_T, FA_INST_D)(void* dst, int64_t n_words) {
+  if (dst == nullptr || n_words < 0 || n_words > (int64_t)fa::kTimelineWgs * fa::kTimelineWords) return FA_ERR_SHAPE;
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(fa::g_timeline), (size_t)n_words * 8, 0, hipMemcpyDeviceToHost) ==
+                 hipSuccess
+             ? FA_OK
+             : FA_ERR_HIP;
+}
+#endif

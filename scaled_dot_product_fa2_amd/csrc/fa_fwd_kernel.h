@@ -190,6 +190,23 @@ constexpr int kPvLeadD256 = 3;  // one fragment less at D = 256, which is at the
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
+#ifdef FA_TIMELINE
+// Timeline build only (a separate library compiled with -DFA_TIMELINE; the kernels of libfa.so have
+// none of this). Per workgroup, words of g_timeline: 0 and 3 the fixed 100 MHz clock
+// (s_memrealtime) at its start and end, 6 and 7 the shader clock (s_memtime) at the same points,
+// 1 and 2 the fixed clock when its first item's Q tile is in registers and when that item's key
+// loop ends, 4 the shader clocks that item spent waiting for tile copies and at the per-tile
+// barrier, 5 that item's key tiles. Written with ordinary vector stores by thread 0.
+constexpr int kTimelineWgs = 65536;
+constexpr int kTimelineWords = 8;
+static __device__ unsigned long long g_timeline[kTimelineWgs * kTimelineWords];
+#define FA_TL_STAMP(word, value)                                                \
+  do {                                                                          \
+    if (threadIdx.x == 0 && blockIdx.x < kTimelineWgs)                          \
+      g_timeline[(size_t)blockIdx.x * kTimelineWords + (word)] = (value);       \
+  } while (0)
+#endif
+
 template <typename T, bool CAUSAL, class Cfg, bool WINDOW = false, bool VARLEN = false>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
@@ -223,6 +240,10 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const Schedule sched{p.B * p.Hkv, p.Hkv, p.group, p.n_qtiles, CAUSAL, (int)gridDim.x};
   const int xcd = blockIdx.x % 8;
   const uint32_t n_mine = sched.items_of(xcd);
+#ifdef FA_TIMELINE
+  FA_TL_STAMP(0, __builtin_amdgcn_s_memrealtime());
+  FA_TL_STAMP(6, __builtin_amdgcn_s_memtime());
+#endif
   for (uint32_t round = 0;; ++round) {
     const uint32_t idx = sched.item_index(blockIdx.x, round);
     if (idx >= n_mine) break;
@@ -303,6 +324,10 @@ __global__ void __launch_bounds__(Cfg::THREADS)
             vec8, lds_read16(qsrc + tile_chunk_offset<D, BKV, false>(row % BKV, kfrag_chunk(s, lane))));
     }
     __syncthreads();  // the Q staging area takes K/V tiles below
+#ifdef FA_TIMELINE
+    if (round == 0) FA_TL_STAMP(1, __builtin_amdgcn_s_memrealtime());
+    unsigned long long tl_wait = 0;
+#endif
 
     // leading tiles in which every (row, key) pair of the workgroup is visible and in range
     int n_full = nkv / BKV;
@@ -347,8 +372,14 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       const bool mask = WINDOW ? !(kpos >= wq_last - p.win_left && kpos + BKV - 1 <= wq_first + p.win_right &&
                                    kpos + BKV <= nkv)
                                : j >= n_full;
+#ifdef FA_TIMELINE
+      const unsigned long long tl_w0 = __builtin_amdgcn_s_memtime();
+#endif
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+#ifdef FA_TIMELINE
+      tl_wait += __builtin_amdgcn_s_memtime() - tl_w0;
+#endif
       if (j + 1 < n_tiles) {
         dma_tile<D, BKV, NW>(knext, kbase, k_stride, kpos + BKV, nkv, wave_u, k_dma_off);
         dma_tile<D, BKV, NW>(vnext, vbase, v_stride, kpos + BKV, nkv, wave_u, v_dma_off);
@@ -539,6 +570,13 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       step(IC<1>(), j + 1);
     }
     if (j < n_tiles) step(IC<0>(), j);
+#ifdef FA_TIMELINE
+    if (round == 0) {
+      FA_TL_STAMP(2, __builtin_amdgcn_s_memrealtime());
+      FA_TL_STAMP(4, tl_wait);
+      FA_TL_STAMP(5, (unsigned long long)n_tiles);
+    }
+#endif
 
     // ---- epilogue: O = acc / l (rounded once to T), LSE = (m + log2 l) * ln 2
     const float LN2 = 0.69314718055994530942f;
@@ -569,6 +607,10 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       }
     }
   }  // item loop
+#ifdef FA_TIMELINE
+  FA_TL_STAMP(3, __builtin_amdgcn_s_memrealtime());
+  FA_TL_STAMP(7, __builtin_amdgcn_s_memtime());
+#endif
 }
 
 }  // namespace fa
