@@ -87,10 +87,16 @@ __device__ __forceinline__ SeqSpan seq_span(const BwdParams& p, int b) {
   return SeqSpan{min(cq1 - cq0, p.Nq), min(ck1 - ck0, p.Nkv), cq0, ck0};
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
+
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // Fragment read-ahead of the gradient kernels, in fragments (as in the forward's loops).
 constexpr int kBwdLead = 3;
+// The transposed reads of the dK/dV form with K and V in LDS, which holds its partial dK and dV at
+// two waves per SIMD and has registers for less read-ahead.
+constexpr int kBwdLeadKvl = 2;
 // The dQ kernel's score loop at D >= 128 under a mask holds the mask's row bounds as well; one
 // fragment less read-ahead there keeps it inside the register file.
 constexpr int kBwdDqMaskedLead = 2;
@@ -122,15 +128,20 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const BwdParams p) {
 }
 
 // Workgroup shape of the gradient kernels: NW waves of 32 rows each (keys for dK/dV, query rows
-// for dQ), tiles of BT rows streamed past them (query rows for dK/dV, keys for dQ).
-template <int D_, int NW_, int BT_, int WAVES_PER_SIMD_>
+// for dQ), tiles of BT rows streamed past them (query rows for dK/dV, keys for dQ). In the KVL form
+// of dK/dV, NW/2 groups of 32 keys with two waves each, one per 32-row half of every tile.
+template <int D_, int NW_, int BT_, int WAVES_PER_SIMD_, bool KVL_ = false>
 struct BwdCfg {
   static constexpr int D = D_;
   static constexpr int NW = NW_;
   static constexpr int BT = BT_;
   static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
+  // dK/dV only: K and V of the workgroup's keys staged in LDS instead of each wave's registers,
+  // and two waves per 32-key group, each taking one 32-row half of every query tile
+  static constexpr bool KVL = KVL_;
+  static constexpr int NKG = KVL ? NW / 2 : NW;  // 32-row groups the workgroup owns
   static constexpr int THREADS = NW * 64;
-  static constexpr int BW = NW * 32;  // rows owned by the workgroup
+  static constexpr int BW = NKG * 32;  // rows owned by the workgroup
   static constexpr int TILE_BYTES = BT * D * 2;
   static_assert(BT % 32 == 0 && dma_insts<D, BT>() * 64 == BT * (D / 8), "tile rows must fill whole copies");
 };
@@ -151,6 +162,9 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   constexpr int NDB = DPAD ? 1 : D / 32;
   constexpr int NQB = BQ / 32;  // 32-row query blocks per tile
   constexpr int TB = Cfg::TILE_BYTES;
+  constexpr bool KVL = Cfg::KVL;
+  constexpr int NKG = Cfg::NKG;
+  static_assert(!KVL || (PART == kBwdBoth && NW == 2 * NKG && NQB == 2), "K/V in LDS: both outputs, two row halves");
   typedef typename Elem<T>::vec8 vec8;
 
   // Q and dO tiles in the transposing layout (read both as row fragments and transposed), two
@@ -163,11 +177,17 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   __shared__ __attribute__((aligned(256))) float ls_st1[BQ];
   __shared__ __attribute__((aligned(256))) float dl_st0[BQ];
   __shared__ __attribute__((aligned(256))) float dl_st1[BQ];
+  // K and V rows of the workgroup's keys (the KVL form; a stub otherwise)
+  constexpr int KVB = KVL ? BK * D * 2 : 16;
+  __shared__ __attribute__((aligned(1024))) char k_lds_raw[KVB];
+  __shared__ __attribute__((aligned(1024))) char v_lds_raw[KVB];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int kg = KVL ? wave % NKG : wave;  // 32-key group of this wave
+  const int rh = KVL ? wave / NKG : 0;     // (KVL) the 32-row half of each query tile it takes
   // 1-D grid over (key block, kv head, batch). Key block slowest: under the causal mask the early
   // key blocks, which see the most query tiles, are dispatched first (longest first). Key block
   // fastest: the key blocks of one head are dispatched together and share its Q/dO stream in cache.
@@ -188,13 +208,13 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const SeqSpan sq = seq_span<VARLEN>(p, b);
   const int nq = sq.nq, nkv = sq.nkv;
   if (VARLEN && k0 >= nkv) return;  // a key block past this sequence's end (workgroup-uniform)
-  const int kw0 = k0 + 32 * wave;  // first key of this wave
+  const int kw0 = k0 + 32 * kg;  // first key of this wave
   const int my_key = kw0 + (lane & 31);
 
   // K and V rows of the wave's keys as B operands: lane holds row (lane % 32), elements
   // 16*s + 8*(lane/32) .. +7. Keys past the sequence read as zero.
   vec8 kf[NS], vf[NS];
-  {
+  if constexpr (!KVL) {
     const T* krow = (const T*)p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)(sq.k_tok0 + my_key) * p.k_sn;
     const T* vrow = (const T*)p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)(sq.k_tok0 + my_key) * p.v_sn;
 #pragma unroll
@@ -263,6 +283,23 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const int t_lane[2] = {vtr_swz_lane_offset<D, BQ>(0, lane), vtr_swz_lane_offset<D, BQ>(1, lane)};
   const float c = p.c;
 
+  // KVL: the workgroup's K and V rows, copied once with the first query tile and read as the same
+  // B-operand fragments the register form holds
+  const lds_char_t* const k_lds = (const lds_char_t*)k_lds_raw;
+  const lds_char_t* const v_lds = (const lds_char_t*)v_lds_raw;
+  int kv_lane[KP];
+#pragma unroll
+  for (int par = 0; par < KP; ++par) kv_lane[par] = KVL ? kfrag_lane_offset<D, BK>(par, lane) : 0;
+  if (KVL && n_work > 0) {
+    const int k_stride = (int)(p.k_sn * 2), v_stride = (int)(p.v_sn * 2);
+    const char* kbase = (const char*)p.k + (b * p.k_sb + kvh * p.k_sh + (int64_t)sq.k_tok0 * p.k_sn) * 2;
+    const char* vbase = (const char*)p.v + (b * p.v_sb + kvh * p.v_sh + (int64_t)sq.k_tok0 * p.v_sn) * 2;
+    dma_tile<D, BK, NW>((lds_char_t*)k_lds_raw, kbase, k_stride, k0, nkv, wave_u,
+                        (int)dma_lane_offset<D, false>(lane, k_stride));
+    dma_tile<D, BK, NW>((lds_char_t*)v_lds_raw, vbase, v_stride, k0, nkv, wave_u,
+                        (int)dma_lane_offset<D, false>(lane, v_stride));
+  }
+
   auto step = [&](auto stage_c, int w) {
     constexpr int S = decltype(stage_c)::value;
     lds_char_t* const qt = (lds_char_t*)(S == 0 ? q_st0_raw : q_st1_raw);
@@ -279,7 +316,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     }
     const int q0 = (qt0 + w % per_head) * BQ;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
+    for (int qi = 0; qi < (KVL ? 1 : NQB); ++qi) {
+      const int qb = KVL ? rh : qi;
       const int qrow0 = q0 + 32 * qb;
       // every query row of the block is before the wave's first key: nothing visible
       if (CAUSAL && qrow0 + 31 < kw0) continue;
@@ -288,25 +326,35 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       if (qrow0 >= nq) continue;
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
       {
-        vec8 qa[NS], oa[NS];
+        vec8 qa[NS], oa[NS], ka[NS], va[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const int off = q_lane[s % KP] + kfrag_const_offset<D, BQ>(qb, s);
           qa[s] = __builtin_bit_cast(vec8, lds_read16(qt + off));
           if (DO_K) oa[s] = __builtin_bit_cast(vec8, lds_read16(ot + off));
+          if (KVL) {
+            const int koff = kv_lane[s % KP] + kfrag_const_offset<D, BK>(kg, s);
+            ka[s] = __builtin_bit_cast(vec8, lds_read16(k_lds + koff));
+            va[s] = __builtin_bit_cast(vec8, lds_read16(v_lds + koff));
+          }
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          s_acc = Elem<T>::mfma(qa[s], kf[s], s_acc);
-          if (DO_K) dp_acc = Elem<T>::mfma(oa[s], vf[s], dp_acc);
+          s_acc = Elem<T>::mfma(qa[s], KVL ? ka[s] : kf[s], s_acc);
+          if (DO_K) dp_acc = Elem<T>::mfma(oa[s], KVL ? va[s] : vf[s], dp_acc);
         }
-        constexpr int PER = DO_K ? 2 : 1;
-        constexpr int LEAD = kBwdLead < NS ? kBwdLead : NS;
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PER * LEAD, 0);
+        // Pinned read-ahead. The KVL form, which reads K and V fragments here as well, is left to
+        // the compiler's pressure-aware placement: pinned, its reads are all hoisted ahead of the
+        // first MFMA and spill.
+        if constexpr (!KVL) {
+          constexpr int PER = DO_K ? 2 : 1;
+          constexpr int LEAD = kBwdLead < NS ? kBwdLead : NS;
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PER * LEAD, 0);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, PER, 0);
-          if (s + LEAD < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PER, 0);
+          for (int s = 0; s < NS; ++s) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, PER, 0);
+            if (s + LEAD < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PER, 0);
+          }
         }
       }
       // register r holds query row qrow0 + acc_row(r, lane) against the lane's key; registers
@@ -363,7 +411,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           }
         constexpr int PER = (DO_V ? 1 : 0) + (DO_K ? 1 : 0);
         constexpr int NF = 2 * NDB;
-        constexpr int LEAD = kBwdLead < NF ? kBwdLead : NF;
+        constexpr int LEAD = (KVL ? kBwdLeadKvl : kBwdLead) < NF ? (KVL ? kBwdLeadKvl : kBwdLead) : NF;
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PER * LEAD, 0);
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
@@ -382,6 +430,42 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   }
   if (w < n_work) step(IC<0>(), w);
 
+  if constexpr (KVL) {
+    // The two row halves of a key group hold partial sums of its dK and dV: the first half keeps dV
+    // and hands its dK over, the second keeps dK and hands its dV over, through 16 KiB exchange
+    // slots carved from the (now idle) tile buffers; each then adds the other's part to its own
+    // (a fixed order, so results repeat) and writes one of the two outputs.
+    static_assert(NDB * 4 * 64 * 16 == 16384 && TB >= 16384 && KVB >= 2 * 16384 && NKG <= 4, "exchange slots");
+    __syncthreads();  // every wave is done with the tiles
+    auto xslot = [&](int i) {
+      lds_char_t* const base = (lds_char_t*)(i < 2 ? k_lds_raw : i < 4 ? v_lds_raw : i == 4 ? q_st0_raw : i == 5 ? q_st1_raw : i == 6 ? o_st0_raw : o_st1_raw);
+      return (lds_f32x4_t*)(base + (i < 4 ? (i & 1) * 16384 : 0));
+    };
+    lds_f32x4_t* const out = xslot(2 * kg + rh);
+    lds_f32x4_t* const in = xslot(2 * kg + 1 - rh);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 give;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) give[e] = rh == 0 ? dkT[db][4 * r4 + e] : dvT[db][4 * r4 + e];
+        out[(db * 4 + r4) * 64 + lane] = give;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 o = in[(db * 4 + r4) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dvT[db][4 * r4 + e] += rh == 0 ? o[e] : 0.f;
+          dkT[db][4 * r4 + e] += rh == 0 ? 0.f : o[e];
+        }
+      }
+  }
+
   // ---- epilogue: lane owns key my_key; register r of block db is head-dim 32*db + acc_row(r)
   if (my_key < nkv) {
     char* dkrow = (char*)p.dk + (b * p.dk_sb + kvh * p.dk_sh + (int64_t)(sq.k_tok0 + my_key) * p.dk_sn) * 2;
@@ -397,8 +481,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           vv[e] = (T)dvT[db][4 * g4 + e];
         }
         const int col = 32 * db + acc_row(4 * g4, lane);
-        if (DO_K) *(i32x2*)(dkrow + col * 2) = __builtin_bit_cast(i32x2, kv);
-        if (DO_V) *(i32x2*)(dvrow + col * 2) = __builtin_bit_cast(i32x2, vv);
+        if (DO_K && (!KVL || rh == 1)) *(i32x2*)(dkrow + col * 2) = __builtin_bit_cast(i32x2, kv);
+        if (DO_V && (!KVL || rh == 0)) *(i32x2*)(dvrow + col * 2) = __builtin_bit_cast(i32x2, vv);
       }
   }
 }

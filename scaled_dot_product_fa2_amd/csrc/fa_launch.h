@@ -29,17 +29,19 @@ template <> struct CfgFor<64> { typedef TileCfg<64, 4, 1, 64, 3> type; };
 template <> struct CfgFor<128> { typedef TileCfg<128, 4, 1, 64, 2> type; };
 template <> struct CfgFor<256> { typedef TileCfg<256, 4, 1, 32, 2> type; };
 
-// Backward, per head dim: the dK/dV kernel (32 keys per wave, 64-row query tiles) and the dQ kernel
-// (32 query rows per wave, 64-key tiles; 32 at D = 256). At D = 256 dV and dK run as two launches
-// (S recomputed in each) so a wave's registers hold one accumulator set, not two; at D = 128 that
-// split measured 15 % slower than one launch at one wave per SIMD. Waves per SIMD: dK/dV two up to
-// D = 64 (and for the split launches up to D = 128), dQ two up to D = 128, otherwise one.
+// Backward, per head dim: the dK/dV kernel (32 keys per wave group, 64-row query tiles) and the dQ
+// kernel (32 query rows per wave, 64-key tiles; 32 at D = 256). At D = 128 the dK/dV workgroup
+// stages its 128 keys' K and V in LDS and runs eight waves, two per 32-key group (one per 32-row
+// half of each query tile), so that it fits two waves per SIMD; below that a wave keeps its keys'
+// K and V in registers at two waves per SIMD. At D = 256 dV and dK run as two launches (S
+// recomputed in each) at one wave per SIMD. dQ: two waves per SIMD up to D = 128, otherwise one.
 template <int D>
 struct BwdCfgFor {
   static constexpr bool SPLIT_KV = D >= 256;
-  static constexpr int W_KV = D <= 64 ? 2 : (SPLIT_KV && D <= 128 ? 2 : 1);
+  static constexpr bool KV_LDS = D == 128;
+  static constexpr int W_KV = D <= 128 ? 2 : 1;
   static constexpr int W_Q = D <= 128 ? 2 : 1;
-  typedef BwdCfg<D, 4, 64, W_KV> dkdv;
+  typedef BwdCfg<D, KV_LDS ? 8 : 4, 64, W_KV, KV_LDS> dkdv;
   typedef BwdCfg<D, 4, D >= 256 ? 32 : 64, W_Q> dq;
 };
 
