@@ -83,10 +83,13 @@ CROSS = [(100, 230), (230, 100), (1, 77), (77, 1), (129, 129)]
 
 @pytest.mark.parametrize("Nq,Nkv", CROSS, ids=[f"{a}x{b}" for a, b in CROSS])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_unequal_lengths(Nq, Nkv, causal):
-    _announce(f"bwd lengths {Nq}x{Nkv} causal={causal}")
-    q, k, v = workloads.make_random(2, 4, 1, Nq, Nkv, 64, torch.bfloat16, seed=Nq * 7 + Nkv)
-    _check(q, k, v, _dout(2, 4, Nq, 64, torch.bfloat16, Nq + Nkv), causal, what=f"{Nq}x{Nkv}")
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_unequal_lengths(Nq, Nkv, causal, D):
+    # D = 128 runs the dK/dV form with K and V in LDS; causal 100 x 230 leaves it a key block that
+    # no query row sees (no tile copied or streamed, zero gradients written after the exchange)
+    _announce(f"bwd lengths {Nq}x{Nkv} causal={causal} D={D}")
+    q, k, v = workloads.make_random(2, 4, 1, Nq, Nkv, D, torch.bfloat16, seed=Nq * 7 + Nkv)
+    _check(q, k, v, _dout(2, 4, Nq, D, torch.bfloat16, Nq + Nkv), causal, what=f"{Nq}x{Nkv} D{D}")
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 1), (6, 3)], ids=["mha", "mqa", "gqa2"])
