@@ -88,6 +88,37 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            float scale, int causal, int dtype, void* stream);
 
 /*
+ * fa_fwd_balanced - fa_fwd for callers that can lend it a small counter buffer, with which long
+ * causal launches even out the uneven clocks of the chip's XCDs. The schedule of fa_fwd gives
+ * every workgroup the same work, so a launch ends when its slowest XCD does; here, in a dense
+ * causal launch at D <= 128 with a key range of at least 128 tiles and at least 8 rounds of items, the last
+ * rounds of each XCD's list (its shortest items) are claimed through the counters instead, and
+ * an XCD that runs out takes items from the one with the most left. The outputs are bitwise those
+ * of fa_fwd: every item is computed the same way whichever workgroup runs it. Other launches use
+ * fa_fwd's schedule and leave the counters alone.
+ *
+ * counters: device pointer to FA_BALANCE_COUNTERS uint32 words, 64-byte aligned, zero before the
+ *           buffer's first use; every call leaves them zero when its kernel ends. Calls that may
+ *           run at the same time (other streams) need buffers of their own; calls in order on one
+ *           stream can share one. FA_ERR_NULL / FA_ERR_LAYOUT for a NULL or misaligned pointer.
+ *
+ * Everything else (arguments, layout, ownership, errors) as in fa_fwd; the library allocates
+ * nothing and keeps no state of its own.
+ */
+#define FA_BALANCE_COUNTERS 16
+
+/* 1 if fa_fwd_balanced would claim items through its counters for this launch (a dense causal
+ * launch at D <= 128 with a key range of at least 128 tiles and at least 8 rounds of items), 0 if it would use
+ * fa_fwd's schedule; a negative FA_ERR_* code for arguments fa_fwd would reject. */
+int fa_fwd_balance_applies(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                           int causal, int dtype);
+int fa_fwd_balanced(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                    const int64_t q_stride[4], const int64_t k_stride[4],
+                    const int64_t v_stride[4], const int64_t o_stride[4],
+                    float scale, int causal, int dtype, uint32_t* counters, void* stream);
+
+/*
  * fa_fwd_window - fa_fwd with a sliding-window mask in place of the causal flag: query row i
  * sees the keys j with i - window_left <= j <= i + window_right (zero-based positions, the same
  * top-left anchoring as the causal mask). window_left / window_right = -1 leaves that side

@@ -5,6 +5,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import threading
 from typing import Optional, Tuple
 
 import torch
@@ -46,6 +47,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p, f32, i32,
                            i32, vp]
     lib.fa_fwd.restype = i32
+    lib.fa_fwd_balanced.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p, f32,
+                                    i32, i32, vp, vp]
+    lib.fa_fwd_balanced.restype = i32
+    lib.fa_fwd_balance_applies.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32]
+    lib.fa_fwd_balance_applies.restype = i32
     lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p, f32,
                                   i64, i64, i32, vp]
     lib.fa_fwd_window.restype = i32
@@ -102,6 +108,15 @@ def fa_fwd_plan(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int, causal: bo
     return {f: getattr(plan, f) for f, _ in _Plan._fields_}
 
 
+def fa_fwd_balance_applies(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int, causal: bool, dtype) -> bool:
+    """Whether the forward of this shape claims the tail of its schedule (see fa_fwd_balanced)."""
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    rc = load_library().fa_fwd_balance_applies(B, Hq, Hkv, Nq, Nkv, D, int(bool(causal)), dt)
+    if rc < 0:
+        raise FaError(rc, fa_strerror(rc))
+    return rc == 1
+
+
 def _strides(t: torch.Tensor):
     return (ctypes.c_int64 * 4)(*t.stride())
 
@@ -123,6 +138,27 @@ def _stream_for(dev: torch.device, stream):
     return stream
 
 
+# fa_fwd_balanced's counter words (FA_BALANCE_COUNTERS in fa.h), one zeroed buffer per (device,
+# stream): calls in order on one stream may share a buffer, calls on different streams may not.
+BALANCE_COUNTERS = 16
+_balance_buffers = {}
+_balance_lock = threading.Lock()
+
+
+def _balance_counters(dev: torch.device, stream) -> torch.Tensor:
+    """The counter buffer of `stream`, zero-filled on that stream on first use (so the fill is ordered
+    before the stream's first forward) and kept for the life of the process; every forward leaves it
+    zero again."""
+    key = (dev.index, stream.cuda_stream)
+    with _balance_lock:
+        buf = _balance_buffers.get(key)
+        if buf is None:
+            with torch.cuda.device(dev), torch.cuda.stream(stream):
+                buf = torch.zeros(BALANCE_COUNTERS, dtype=torch.int32, device=dev)
+            _balance_buffers[key] = buf
+    return buf
+
+
 def _call_on(dev: torch.device, fn, *args) -> int:
     """Call a library entry point with `dev` as the current device. A launch on a null stream handle
     (the default stream) goes to the current device, and fa_bwd_noalloc looks up its array there, so
@@ -134,14 +170,15 @@ def _call_on(dev: torch.device, fn, *args) -> int:
 
 
 class FaCall:
-    """A validated, pre-marshalled fa_fwd call on fixed tensors: calling it enqueues one forward.
+    """A validated, pre-marshalled forward call on fixed tensors: calling it enqueues one forward
+    (through fa_fwd_balanced, like ``fa_fwd``).
 
     Built by ``fa_fwd_call``; the ctypes argument tuple is prepared once, so repeated launches cost
     only the foreign call. The tensors must stay alive and keep their storage while it is used.
     """
 
     def __init__(self, dev, args, keepalive):
-        self._fn = load_library().fa_fwd
+        self._fn = load_library().fa_fwd_balanced
         self._dev = dev
         self._args = args
         self._keepalive = keepalive
@@ -163,11 +200,12 @@ def fa_fwd_call(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
         scale = 1.0 / math.sqrt(D)
     stream = _stream_for(q.device, stream)
     strides = [_strides(t) for t in (q, k, v, out)]
+    counters = _balance_counters(q.device, stream)
     args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
             ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
             B, Hq, Hkv, Nq, Nkv, D, *strides, ctypes.c_float(scale), int(bool(causal)), _DTYPES[q.dtype],
-            ctypes.c_void_p(stream.cuda_stream))
-    return FaCall(q.device, args, (q, k, v, out, lse, strides))
+            ctypes.c_void_p(counters.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+    return FaCall(q.device, args, (q, k, v, out, lse, strides, counters))
 
 
 class FaBwdCall:
@@ -214,7 +252,9 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = 
     q: (B, Hq, Nq, D); k, v: (B, Hkv, Nkv, D); fp16 or bf16 on one GPU; any strides with a unit
     head-dim stride and 16-byte aligned rows. ``scale`` defaults to 1/sqrt(D). ``out`` (same shape
     and dtype as q) and ``lse`` (contiguous float32 (B, Hq, Nq)) may be passed in; otherwise they are
-    allocated. The kernel is enqueued on ``stream`` (default: the current stream).
+    allocated. The kernel is enqueued on ``stream`` (default: the current stream), through
+    fa_fwd_balanced with the stream's counter buffer: long causal launches then even out the XCDs'
+    uneven clocks, with outputs bitwise those of fa_fwd.
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, H, N, D)")
@@ -239,10 +279,12 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = 
         raise ValueError("lse must be a contiguous float32 (B, Hq, Nq) tensor")
     _on_device(q.device, out=out, lse=lse)
     stream = _stream_for(q.device, stream)
+    counters = _balance_counters(q.device, stream)
     code = _call_on(
-        q.device, load_library().fa_fwd, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-        B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(out),
-        float(scale), int(bool(causal)), _DTYPES[q.dtype], ctypes.c_void_p(stream.cuda_stream))
+        q.device, load_library().fa_fwd_balanced, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, _strides(q), _strides(k), _strides(v), _strides(out),
+        float(scale), int(bool(causal)), _DTYPES[q.dtype], ctypes.c_void_p(counters.data_ptr()),
+        ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return out, lse
 

@@ -4,6 +4,7 @@
 // every entry point are in include/fa.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -94,16 +95,37 @@ int check_strides(const int64_t* st, bool is_output, int64_t B, int64_t H, int64
   return FA_OK;
 }
 
-template <typename T, bool CAUSAL, bool WINDOW = false, bool VARLEN = false>
+template <typename T, bool CAUSAL, bool WINDOW = false, bool VARLEN = false, bool BALANCED = false>
 int launch_d(int64_t D, const FwdParams& p, int64_t grid, hipStream_t stream) {
   switch (D) {
-    case 16: return fa::launch_fwd<T, CAUSAL, 16, WINDOW, VARLEN>(p, grid, stream);
-    case 32: return fa::launch_fwd<T, CAUSAL, 32, WINDOW, VARLEN>(p, grid, stream);
-    case 64: return fa::launch_fwd<T, CAUSAL, 64, WINDOW, VARLEN>(p, grid, stream);
-    case 128: return fa::launch_fwd<T, CAUSAL, 128, WINDOW, VARLEN>(p, grid, stream);
-    case 256: return fa::launch_fwd<T, CAUSAL, 256, WINDOW, VARLEN>(p, grid, stream);
+    case 16: return fa::launch_fwd<T, CAUSAL, 16, WINDOW, VARLEN, BALANCED>(p, grid, stream);
+    case 32: return fa::launch_fwd<T, CAUSAL, 32, WINDOW, VARLEN, BALANCED>(p, grid, stream);
+    case 64: return fa::launch_fwd<T, CAUSAL, 64, WINDOW, VARLEN, BALANCED>(p, grid, stream);
+    case 128: return fa::launch_fwd<T, CAUSAL, 128, WINDOW, VARLEN, BALANCED>(p, grid, stream);
+    case 256: return fa::launch_fwd<T, CAUSAL, 256, WINDOW, VARLEN, BALANCED>(p, grid, stream);
     default: return FA_ERR_HEAD_DIM;
   }
+}
+
+// Whether a dense launch takes the balanced instance: under the causal mask, at D <= 128, with a
+// key range of at least kBalanceMinKvTiles tiles and at least kBalanceMinRounds rounds of items on
+// some XCD. Shorter launches lose more to the claims, and to the long/short pairing the claimed
+// tail gives up, than the uneven XCD clocks cost them; at D = 256 (32-key tiles, 16 MiB of K and V
+// per unit at N = 16384) a stolen item's cold K/V stream costs more than it saves.
+static_assert(fa::kBalanceCounters == FA_BALANCE_COUNTERS, "counter buffer size");
+constexpr int64_t kBalanceMinKvTiles = 128;
+constexpr uint32_t kBalanceMinRounds = 8;
+
+bool use_balance(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nkv, int64_t D, int64_t n_qt, int64_t grid, int bkv,
+                 bool causal) {
+  if (!causal || D > 128 || (Nkv + bkv - 1) / bkv < kBalanceMinKvTiles) return false;
+  const fa::Schedule sched{(int)(B * Hkv), (int)Hkv, (int)(Hq / Hkv), (int)n_qt, true, (int)grid};
+  uint32_t rounds = 0;
+  for (int x = 0; x < 8; ++x) {
+    const int gx = sched.wgs_of(x);
+    if (gx > 0) rounds = std::max(rounds, (sched.items_of(x) + (uint32_t)gx - 1) / (uint32_t)gx);
+  }
+  return rounds >= kBalanceMinRounds;
 }
 
 // Shared validation and parameter setup of the forward entry points.
@@ -152,6 +174,7 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   p->total_k = 0;
   p->lse_sb = Hq * Nq;
   p->lse_sh = Nq;
+  p->balance = nullptr;
   return FA_OK;
 }
 
@@ -259,6 +282,40 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (dtype == FA_DTYPE_BF16)
     return cz ? launch_d<__bf16, true>(D, p, grid, s) : launch_d<__bf16, false>(D, p, grid, s);
   return cz ? launch_d<_Float16, true>(D, p, grid, s) : launch_d<_Float16, false>(D, p, grid, s);
+}
+
+int fa_fwd_balance_applies(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal,
+                           int dtype) {
+  PlanInfo pi;
+  int64_t n_qt = 0, grid = 0;
+  const int rc = check_shape(B, Hq, Hkv, Nq, Nkv, D, dtype, causal != 0, &pi, &n_qt, &grid);
+  if (rc != FA_OK) return rc;
+  return use_balance(B, Hq, Hkv, Nkv, D, n_qt, grid, pi.bkv, causal != 0) ? 1 : 0;
+}
+
+int fa_fwd_balanced(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                    int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, const int64_t q_stride[4],
+                    const int64_t k_stride[4], const int64_t v_stride[4], const int64_t o_stride[4], float scale,
+                    int causal, int dtype, uint32_t* counters, void* stream) {
+  if (!counters) return FA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(counters) & 63u) != 0) return FA_ERR_LAYOUT;
+  FwdParams p;
+  int64_t grid = 0;
+  const int rc = prepare_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride, scale,
+                             causal != 0, dtype, &p, &grid);
+  if (rc != FA_OK) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PlanInfo pi;
+  plan_for_d(D, &pi);
+  if (!use_balance(B, Hq, Hkv, Nkv, D, p.n_qtiles, grid, pi.bkv, causal != 0)) {
+    const bool cz = causal != 0;
+    if (dtype == FA_DTYPE_BF16)
+      return cz ? launch_d<__bf16, true>(D, p, grid, s) : launch_d<__bf16, false>(D, p, grid, s);
+    return cz ? launch_d<_Float16, true>(D, p, grid, s) : launch_d<_Float16, false>(D, p, grid, s);
+  }
+  p.balance = counters;
+  if (dtype == FA_DTYPE_BF16) return launch_d<__bf16, true, false, false, true>(D, p, grid, s);
+  return launch_d<_Float16, true, false, false, true>(D, p, grid, s);
 }
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,

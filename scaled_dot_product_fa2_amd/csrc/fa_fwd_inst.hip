@@ -11,11 +11,11 @@
 
 namespace fa {
 
-template <typename T, bool CAUSAL, int D, bool WINDOW, bool VARLEN>
+template <typename T, bool CAUSAL, int D, bool WINDOW, bool VARLEN, bool BALANCED>
 int launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream) {
   typedef typename CfgFor<D>::type C;
-  hipLaunchKernelGGL((fa_fwd_kernel<T, CAUSAL, C, WINDOW, VARLEN>), dim3((unsigned)grid), dim3(C::THREADS), 0,
-                     stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<T, CAUSAL, C, WINDOW, VARLEN, BALANCED>), dim3((unsigned)grid), dim3(C::THREADS),
+                     0, stream, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -30,6 +30,7 @@ template int launch_fwd<InstT, true, FA_INST_D, false, false>(const FwdParams&, 
 template int launch_fwd<InstT, false, FA_INST_D, true, false>(const FwdParams&, int64_t, hipStream_t);
 template int launch_fwd<InstT, false, FA_INST_D, false, true>(const FwdParams&, int64_t, hipStream_t);
 template int launch_fwd<InstT, true, FA_INST_D, false, true>(const FwdParams&, int64_t, hipStream_t);
+template int launch_fwd<InstT, true, FA_INST_D, false, false, true>(const FwdParams&, int64_t, hipStream_t);
 
 }  // namespace fa
 

@@ -106,7 +106,20 @@ struct FwdParams {
   const int32_t* cu_k;
   int32_t total_q, total_k;
   int64_t lse_sb, lse_sh;  // LSE element offset of (b, h); the row index is added to it
+  // balanced instances only: claim counters, zero on entry and left zero on exit (kBalanceCounters)
+  uint32_t* balance;
 };
+
+// Balanced instances (dense causal launches with long key ranges and many rounds of items). The
+// XCDs of one chip hold different shader clocks under load, so a schedule that gives every
+// workgroup the same work ends when the slowest XCD does. In these instances each XCD runs the
+// static schedule below for all but the last kBalanceTailRounds rounds of its list (the shortest
+// items, the list being longest first); those are claimed from a per-XCD counter, the next claim
+// issued while the current item runs, and a workgroup whose own XCD has none left takes them from
+// the XCD with the most left. Counter words: 0..7 the claims of each XCD's tail, 8 the workgroups
+// that have finished; the last one to finish zeroes them all.
+constexpr uint32_t kBalanceTailRounds = 3;
+constexpr int kBalanceCounters = 16;
 
 // Tile configuration: NW waves per workgroup, QB 32-row query blocks per wave,
 // BKV keys per inner-loop tile.
@@ -207,7 +220,7 @@ static __device__ unsigned long long g_timeline[kTimelineWgs * kTimelineWords];
   } while (0)
 #endif
 
-template <typename T, bool CAUSAL, class Cfg, bool WINDOW = false, bool VARLEN = false>
+template <typename T, bool CAUSAL, class Cfg, bool WINDOW = false, bool VARLEN = false, bool BALANCED = false>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
     fa_fwd_kernel(const FwdParams p) {
@@ -244,10 +257,88 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   FA_TL_STAMP(0, __builtin_amdgcn_s_memrealtime());
   FA_TL_STAMP(6, __builtin_amdgcn_s_memtime());
 #endif
+  static_assert(!BALANCED || (!WINDOW && !VARLEN), "balanced instances: dense launches only");
+  // (BALANCED) static rounds of XCD y's list: all but the last min(kBalanceTailRounds, rounds - 1)
+  auto head_items_of = [&](int y) -> uint32_t {
+    const uint32_t gy = (uint32_t)sched.wgs_of(y);
+    if (gy == 0) return 0;
+    const uint32_t r = (sched.items_of(y) + gy - 1) / gy;
+    if (r == 0) return 0;
+    const uint32_t t = r - 1 < kBalanceTailRounds ? r - 1 : kBalanceTailRounds;
+    return (r - t) * gy;
+  };
+  __shared__ int s_claim[2];
+  uint32_t my_head_rounds = 0, my_head_items = 0;
+  if constexpr (BALANCED) {
+    my_head_items = head_items_of(xcd);
+    my_head_rounds = my_head_items / (uint32_t)sched.wgs_of(xcd);
+  }
+  int steal_from = 0;  // (thread 0) 0 while the own XCD's tail has items, then 1
+  uint32_t pre = 0;    // (thread 0) an own-tail claim issued one item ahead
+  bool pre_valid = false;
   for (uint32_t round = 0;; ++round) {
-    const uint32_t idx = sched.item_index(blockIdx.x, round);
-    if (idx >= n_mine) break;
-    const Item item = sched.item(xcd, idx);
+    uint32_t idx;
+    int ix = xcd;  // the XCD whose list the item comes from
+    if (!BALANCED || round < my_head_rounds) {
+      idx = sched.item_index(blockIdx.x, round);
+      if (idx >= n_mine) break;
+    } else {
+      if (tid == 0) {
+        int got_x = -1;
+        uint32_t got = 0;
+        if (steal_from == 0) {
+          if (my_head_items < n_mine) {
+            const uint32_t cl = pre_valid ? pre : __hip_atomic_fetch_add(&p.balance[xcd], 1u, __ATOMIC_RELAXED,
+                                                                         __HIP_MEMORY_SCOPE_AGENT);
+            pre_valid = false;
+            if (my_head_items + cl < n_mine) {
+              got_x = xcd;
+              got = my_head_items + cl;
+            }
+          }
+          if (got_x < 0) steal_from = 1;
+        }
+        // the XCD with the most unclaimed items (all eight counters read at once). A claim fails
+        // only on a tail this thread then sees exhausted, so the loop ends within eight failures.
+        for (int attempt = 0; got_x < 0 && attempt < 64; ++attempt) {
+          uint32_t cnt[8];
+#pragma unroll
+          for (int y = 0; y < 8; ++y) cnt[y] = __hip_atomic_load(&p.balance[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          int best = -1;
+          uint32_t best_rem = 0;
+#pragma unroll
+          for (int y = 0; y < 8; ++y) {
+            const uint32_t ny = sched.items_of(y), hy = head_items_of(y);
+            const uint32_t rem = hy + cnt[y] < ny ? ny - hy - cnt[y] : 0;
+            if (rem > best_rem) {
+              best_rem = rem;
+              best = y;
+            }
+          }
+          if (best < 0) break;
+          const uint32_t cl = __hip_atomic_fetch_add(&p.balance[best], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (head_items_of(best) + cl < sched.items_of(best)) {
+            got_x = best;
+            got = head_items_of(best) + cl;
+          }
+        }
+        s_claim[0] = got_x;
+        s_claim[1] = (int)got;
+      }
+      __syncthreads();
+      ix = s_claim[0];
+      idx = (uint32_t)s_claim[1];
+      __syncthreads();  // s_claim is read by every wave before thread 0 writes it again
+      if (ix < 0) break;
+    }
+    const Item item = sched.item(ix, idx);
+    if constexpr (BALANCED) {
+      // claim the next own-tail item while this one runs, from the last static round on
+      if (tid == 0 && steal_from == 0 && !pre_valid && round + 1 >= my_head_rounds && my_head_items < n_mine) {
+        pre = __hip_atomic_fetch_add(&p.balance[xcd], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pre_valid = true;
+      }
+    }
     const int b = item.b, h = item.h, qt = item.qt;
     const int kvh = h / p.group;
     const int q0 = qt * BQ;
@@ -607,6 +698,16 @@ __global__ void __launch_bounds__(Cfg::THREADS)
       }
     }
   }  // item loop
+  if constexpr (BALANCED) {
+    if (tid == 0) {
+      // every workgroup's claims are done before it counts itself finished, so the last one to
+      // finish can zero the counters for the next launch
+      const uint32_t done = __hip_atomic_fetch_add(&p.balance[8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == gridDim.x - 1) {
+        for (int y = 0; y < 9; ++y) __hip_atomic_store(&p.balance[y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
 #ifdef FA_TIMELINE
   FA_TL_STAMP(3, __builtin_amdgcn_s_memrealtime());
   FA_TL_STAMP(7, __builtin_amdgcn_s_memtime());

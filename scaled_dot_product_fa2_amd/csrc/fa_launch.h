@@ -45,8 +45,9 @@ struct BwdCfgFor {
   typedef BwdCfg<D, 4, D >= 256 ? 32 : 64, W_Q> dq;
 };
 
-// Enqueue one forward instance on `stream` with a 1-D grid of `grid` workgroups.
-template <typename T, bool CAUSAL, int D, bool WINDOW, bool VARLEN>
+// Enqueue one forward instance on `stream` with a 1-D grid of `grid` workgroups (BALANCED: the
+// instance with the claimed tail, dense causal only; p.balance must then hold the counters).
+template <typename T, bool CAUSAL, int D, bool WINDOW, bool VARLEN, bool BALANCED = false>
 int launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream);
 
 // Enqueue the backward's kernels (Delta, dK/dV, dQ) of one instance on `stream`.

@@ -98,6 +98,61 @@ def test_validation_rejects(name, over, code):
     assert _call(**over) == D_[code]
 
 
+def _call_balanced(counters=0x60000, **over):
+    a = dict(VALID)
+    a.update(over)
+    return _lib().fa_fwd_balanced(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                  a["Nkv"], a["D"], _st(*a["qs"]) if a["qs"] else None,
+                                  _st(*a["ks"]) if a["ks"] else None, _st(*a["vs"]) if a["vs"] else None,
+                                  _st(*a["os"]) if a["os"] else None, a["scale"], a["causal"], a["dtype"],
+                                  counters, None)
+
+
+@pytest.mark.parametrize("name,over,code", BAD, ids=[b[0] for b in BAD])
+def test_balanced_validation_rejects(name, over, code):
+    # fa_fwd_balanced validates exactly as fa_fwd, before any HIP call
+    assert _call_balanced(**over) == D_[code]
+
+
+# (B, Hq, Hkv, N, D, causal, expected): the balanced entry point claims the tail only of dense causal
+# launches at D <= 128 with >= 128 key tiles and >= 8 rounds of items on an XCD
+BALANCE_POLICY = [
+    ((4, 16, 16, 1024, 128), True, 0),     # the benchmark shape: one round, 16 key tiles
+    ((4, 16, 16, 1024, 128), False, 0),
+    ((1, 32, 8, 16384, 128), True, 1),     # the long GQA workload: 8 rounds, 256 key tiles
+    ((1, 32, 8, 16384, 128), False, 0),    # no mask: every item the same length
+    ((2, 16, 16, 4096, 256), True, 0),     # the D = 256 workload: 2 rounds
+    ((128, 8, 8, 1024, 64), True, 0),      # many rounds, 16 key tiles
+    ((4, 16, 16, 8192, 128), True, 1),     # exactly 8 rounds and 128 key tiles
+    ((4, 16, 16, 4096, 128), True, 0),     # 4 rounds
+    ((2, 16, 16, 16384, 256), True, 0),    # 8 rounds, but D = 256: a stolen item's K/V stream costs more
+    ((4, 16, 16, 16384, 64), True, 1),     # D = 64: 11 rounds, 256 key tiles
+]
+
+
+@pytest.mark.parametrize("shape,causal,want", BALANCE_POLICY,
+                         ids=[f"b{s[0]}h{s[1]}kv{s[2]}n{s[3]}d{s[4]}-{'c' if c else 'n'}" for s, c, _ in BALANCE_POLICY])
+def test_balance_policy(shape, causal, want):
+    B, Hq, Hkv, N, D = shape
+    assert _lib().fa_fwd_balance_applies(B, Hq, Hkv, N, N, D, int(causal), 1) == want
+    assert _lib().fa_fwd_balance_applies(B, Hq, Hkv, N, N, D, int(causal), 0) == want
+
+
+def test_balance_policy_rejects_what_fa_fwd_rejects():
+    assert _lib().fa_fwd_balance_applies(1, 2, 1, 128, 128, 48, 1, 1) == D_["FA_ERR_HEAD_DIM"]
+    assert _lib().fa_fwd_balance_applies(1, 3, 2, 128, 128, 64, 1, 1) == D_["FA_ERR_GQA"]
+    assert _lib().fa_fwd_balance_applies(1, 2, 1, 128, 128, 64, 1, 9) == D_["FA_ERR_DTYPE"]
+
+
+def test_balanced_counter_buffer_is_checked():
+    from scaled_dot_product_fa2_amd import _binding
+    assert D_["FA_BALANCE_COUNTERS"] == _binding.BALANCE_COUNTERS
+    assert _call_balanced(counters=0) == D_["FA_ERR_NULL"]
+    assert _call_balanced(counters=0x60004) == D_["FA_ERR_LAYOUT"]  # 64-byte alignment
+    # and the counter checks come first: a bad buffer is reported even with a bad shape
+    assert _call_balanced(counters=0, D=48) == D_["FA_ERR_NULL"]
+
+
 def test_plan_and_tile_pairs():
     from scaled_dot_product_fa2_amd import fa_fwd_plan, fa_tile_pairs
     p = fa_fwd_plan(4, 16, 16, 1024, 1024, 128, False, 1)
