@@ -297,8 +297,10 @@ def timeline(w, warmup_ms: float) -> None:
     """--timeline: one forward launch per mask through libfa_timeline.so (the same kernels with
     per-workgroup clock stamps), after back-to-back launches of the same mask for at least
     `warmup_ms` (the clock settles over tens of milliseconds of load); prints one JSON line with the
-    shader clock the waves held (s_memtime against s_memrealtime over each workgroup's life) and the
-    phases of each workgroup's first item, as median and range over workgroups."""
+    shader clock the waves held (s_memtime against s_memrealtime over each workgroup's life), the
+    phases of each workgroup's first item, as median and range over workgroups, and each XCD's
+    clock and finish times. A launch that the binding sends down the balanced path is stamped once
+    more through fa_fwd itself ("causal_static_schedule"), to show what the balancing evens out."""
     import ctypes
 
     import numpy as np
@@ -318,11 +320,32 @@ def timeline(w, warmup_ms: float) -> None:
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
     rec = {"workload": w.name, "kernel_sha": kernel_sha(), "warmup_ms": warmup_ms, "modes": {}}
+
+    def static_call(o, lse, c):
+        # fa_fwd itself (the static schedule), for launches the binding sends down the balanced path
+        lib = _binding._lib
+        st = [(ctypes.c_int64 * 4)(*t.stride()) for t in (q, k, v, o)]
+        args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(lse.data_ptr()), w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
+                *st, ctypes.c_float(1.0 / math.sqrt(w.D)), int(c), 1 if w.dtype_name == "bf16" else 0,
+                ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+
+        def run():
+            rc = lib.fa_fwd(*args)
+            if rc != 0:
+                raise RuntimeError(_binding.fa_strerror(rc))
+        return run
+
+    runs = []
     for c in w.causal_modes:
+        runs.append(("causal" if c else "non_causal", c, None))
+        if fa.fa_fwd_balance_applies(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, c, w.dtype):
+            runs.append(("causal_static_schedule", c, static_call))
+    for mode, c, make_static in runs:
         grid = fa.fa_fwd_plan(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, c, w.dtype)["grid"]
         o = torch.empty(w.B, w.Hq, w.Nq, w.D, dtype=w.dtype, device=dev)
         lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=dev)
-        call = fa.fa_fwd_call(q, k, v, o, lse, causal=c)
+        call = fa.fa_fwd_call(q, k, v, o, lse, causal=c) if make_static is None else make_static(o, lse, c)
         t0 = time.perf_counter()
         while (time.perf_counter() - t0) * 1e3 < warmup_ms:
             for _ in range(10):
@@ -344,8 +367,12 @@ def timeline(w, warmup_ms: float) -> None:
             return {"median": round(float(np.median(x)), 2), "min": round(float(np.min(x)), 2),
                     "max": round(float(np.max(x)), 2)}
 
-        rec["modes"]["causal" if c else "non_causal"] = {
+        xcd = np.arange(grid) % 8  # workgroups are dealt to the XCDs round-robin
+        rec["modes"][mode] = {
             "workgroups": grid, "span_us": round(float(us[:, 3].max()), 2),
+            "xcd": {"sclk_mhz_median": [round(float(np.median(mhz[xcd == i])), 1) for i in range(8)],
+                    "end_us_median": [round(float(np.median(us[xcd == i, 3])), 2) for i in range(8)],
+                    "end_us_max": [round(float(us[xcd == i, 3].max()), 2) for i in range(8)]},
             "sclk_mhz_median": round(float(np.median(mhz)), 1), "sclk_mhz": stat(mhz),
             "start_us": stat(us[:, 0]), "first_item_prologue_us": stat(us[:, 1] - us[:, 0]),
             "first_item_loop_us": stat(us[:, 2] - us[:, 1]), "end_us": stat(us[:, 3]),

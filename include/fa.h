@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7
+#define FA_ABI_VERSION 8
 
 /* Element types of Q, K, V and O (all four share one type). */
 #define FA_DTYPE_F16 0
