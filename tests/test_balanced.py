@@ -97,6 +97,21 @@ def test_static_launches_leave_counters_untouched(shape, causal):
     assert (counters == 7).all(), "a launch on the static schedule touched the counters"
 
 
+def test_balanced_ragged_unequal_lengths():
+    """A launch that takes the claimed tail with Nq != Nkv, neither a tile multiple."""
+    B, Hq, Hkv, Nq, Nkv, D = 4, 16, 16, 8100, 12345, 128
+    assert _binding.fa_fwd_balance_applies(B, Hq, Hkv, Nq, Nkv, D, True, torch.bfloat16)
+    q, k, v = (t.to(DEV) for t in workloads.make_random(B, Hq, Hkv, Nq, Nkv, D, torch.bfloat16, seed=4400))
+    stream = torch.cuda.current_stream(DEV)
+    counters = torch.zeros(_binding.BALANCE_COUNTERS, dtype=torch.int32, device=DEV)
+    o_ref, l_ref = _static(q, k, v, True, stream)
+    for _ in range(2):
+        o, lse = _balanced(q, k, v, True, counters, stream)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+        assert not counters.any()
+
+
 def test_two_streams_with_their_own_buffers():
     """Two streams run balanced launches at the same time, each with its own counters."""
     q, k, v = _inputs(4, 16, 16, 8192, 128, torch.bfloat16, seed=4200)
