@@ -300,7 +300,7 @@ def timeline(w, warmup_ms: float) -> None:
     shader clock the waves held (s_memtime against s_memrealtime over each workgroup's life), the
     phases of each workgroup's first item, as median and range over workgroups, and each XCD's
     clock and finish times. A launch that the binding sends down the balanced path is stamped once
-    more through fa_fwd itself ("causal_static_schedule"), to show what the balancing evens out."""
+    more through fa_fwd itself ("<mask>_static_schedule"), to show what the balancing evens out."""
     import ctypes
 
     import numpy as np
@@ -338,9 +338,10 @@ def timeline(w, warmup_ms: float) -> None:
 
     runs = []
     for c in w.causal_modes:
-        runs.append(("causal" if c else "non_causal", c, None))
+        mode = "causal" if c else "non_causal"
+        runs.append((mode, c, None))
         if fa.fa_fwd_balance_applies(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, c, w.dtype):
-            runs.append(("causal_static_schedule", c, static_call))
+            runs.append((mode + "_static_schedule", c, static_call))
     for mode, c, make_static in runs:
         grid = fa.fa_fwd_plan(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, c, w.dtype)["grid"]
         o = torch.empty(w.B, w.Hq, w.Nq, w.D, dtype=w.dtype, device=dev)

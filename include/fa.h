@@ -91,7 +91,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * fa_fwd_balanced - fa_fwd for callers that can lend it a small counter buffer, with which long
  * causal launches even out the uneven clocks of the chip's XCDs. The schedule of fa_fwd gives
  * every workgroup the same work, so a launch ends when its slowest XCD does; here, in a dense
- * causal launch at D <= 128 with a key range of at least 128 tiles and at least 8 rounds of items, the last
+ * launch (either mask) at D <= 128 with a key range of at least 128 tiles and at least 8 rounds of items, the last
  * rounds of each XCD's list (its shortest items) are claimed through the counters instead, and
  * an XCD that runs out takes items from the one with the most left. The outputs are bitwise those
  * of fa_fwd: every item is computed the same way whichever workgroup runs it. Other launches use
@@ -107,8 +107,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 #define FA_BALANCE_COUNTERS 16
 
-/* 1 if fa_fwd_balanced would claim items through its counters for this launch (a dense causal
- * launch at D <= 128 with a key range of at least 128 tiles and at least 8 rounds of items), 0 if it would use
+/* 1 if fa_fwd_balanced would claim items through its counters for this launch (a dense launch
+ * at D <= 128 with a key range of at least 128 tiles and at least 8 rounds of items), 0 if it would use
  * fa_fwd's schedule; a negative FA_ERR_* code for arguments fa_fwd would reject. */
 int fa_fwd_balance_applies(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
                            int causal, int dtype);

@@ -107,19 +107,20 @@ int launch_d(int64_t D, const FwdParams& p, int64_t grid, hipStream_t stream) {
   }
 }
 
-// Whether a dense launch takes the balanced instance: under the causal mask, at D <= 128, with a
-// key range of at least kBalanceMinKvTiles tiles and at least kBalanceMinRounds rounds of items on
-// some XCD. Shorter launches lose more to the claims, and to the long/short pairing the claimed
-// tail gives up, than the uneven XCD clocks cost them; at D = 256 (32-key tiles, 16 MiB of K and V
-// per unit at N = 16384) a stolen item's cold K/V stream costs more than it saves.
+// Whether a dense launch takes the balanced instance: at D <= 128, with a key range of at least
+// kBalanceMinKvTiles tiles and at least kBalanceMinRounds rounds of items on some XCD, with or
+// without the causal mask. Shorter launches lose more to the claims, and under the mask to the
+// long/short pairing the claimed tail gives up, than the uneven XCD clocks cost them; at D = 256
+// (32-key tiles, 16 MiB of K and V per unit at N = 16384) a stolen item's cold K/V stream costs
+// more than it saves.
 static_assert(fa::kBalanceCounters == FA_BALANCE_COUNTERS, "counter buffer size");
 constexpr int64_t kBalanceMinKvTiles = 128;
 constexpr uint32_t kBalanceMinRounds = 8;
 
 bool use_balance(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nkv, int64_t D, int64_t n_qt, int64_t grid, int bkv,
                  bool causal) {
-  if (!causal || D > 128 || (Nkv + bkv - 1) / bkv < kBalanceMinKvTiles) return false;
-  const fa::Schedule sched{(int)(B * Hkv), (int)Hkv, (int)(Hq / Hkv), (int)n_qt, true, (int)grid};
+  if (D > 128 || (Nkv + bkv - 1) / bkv < kBalanceMinKvTiles) return false;
+  const fa::Schedule sched{(int)(B * Hkv), (int)Hkv, (int)(Hq / Hkv), (int)n_qt, causal, (int)grid};
   uint32_t rounds = 0;
   for (int x = 0; x < 8; ++x) {
     const int gx = sched.wgs_of(x);
@@ -314,8 +315,12 @@ int fa_fwd_balanced(const void* q, const void* k, const void* v, void* o, float*
     return cz ? launch_d<_Float16, true>(D, p, grid, s) : launch_d<_Float16, false>(D, p, grid, s);
   }
   p.balance = counters;
-  if (dtype == FA_DTYPE_BF16) return launch_d<__bf16, true, false, false, true>(D, p, grid, s);
-  return launch_d<_Float16, true, false, false, true>(D, p, grid, s);
+  if (causal) {
+    if (dtype == FA_DTYPE_BF16) return launch_d<__bf16, true, false, false, true>(D, p, grid, s);
+    return launch_d<_Float16, true, false, false, true>(D, p, grid, s);
+  }
+  if (dtype == FA_DTYPE_BF16) return launch_d<__bf16, false, false, false, true>(D, p, grid, s);
+  return launch_d<_Float16, false, false, false, true>(D, p, grid, s);
 }
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,

@@ -31,6 +31,7 @@ template int launch_fwd<InstT, false, FA_INST_D, true, false>(const FwdParams&, 
 template int launch_fwd<InstT, false, FA_INST_D, false, true>(const FwdParams&, int64_t, hipStream_t);
 template int launch_fwd<InstT, true, FA_INST_D, false, true>(const FwdParams&, int64_t, hipStream_t);
 template int launch_fwd<InstT, true, FA_INST_D, false, false, true>(const FwdParams&, int64_t, hipStream_t);
+template int launch_fwd<InstT, false, FA_INST_D, false, false, true>(const FwdParams&, int64_t, hipStream_t);
 
 }  // namespace fa
 

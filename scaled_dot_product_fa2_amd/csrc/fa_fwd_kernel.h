@@ -110,7 +110,7 @@ struct FwdParams {
   uint32_t* balance;
 };
 
-// Balanced instances (dense causal launches with long key ranges and many rounds of items). The
+// Balanced instances (dense launches with long key ranges and many rounds of items). The
 // XCDs of one chip hold different shader clocks under load, so a schedule that gives every
 // workgroup the same work ends when the slowest XCD does. In these instances each XCD runs the
 // static schedule below for all but the last kBalanceTailRounds rounds of its list (the shortest

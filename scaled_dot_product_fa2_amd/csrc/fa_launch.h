@@ -46,7 +46,7 @@ struct BwdCfgFor {
 };
 
 // Enqueue one forward instance on `stream` with a 1-D grid of `grid` workgroups (BALANCED: the
-// instance with the claimed tail, dense causal only; p.balance must then hold the counters).
+// instance with the claimed tail, dense launches only; p.balance must then hold the counters).
 template <typename T, bool CAUSAL, int D, bool WINDOW, bool VARLEN, bool BALANCED = false>
 int launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream);
 

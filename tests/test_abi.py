@@ -114,17 +114,19 @@ def test_balanced_validation_rejects(name, over, code):
     assert _call_balanced(**over) == D_[code]
 
 
-# (B, Hq, Hkv, N, D, causal, expected): the balanced entry point claims the tail only of dense causal
+# (B, Hq, Hkv, N, D, causal, expected): the balanced entry point claims the tail only of dense
 # launches at D <= 128 with >= 128 key tiles and >= 8 rounds of items on an XCD
 BALANCE_POLICY = [
     ((4, 16, 16, 1024, 128), True, 0),     # the benchmark shape: one round, 16 key tiles
     ((4, 16, 16, 1024, 128), False, 0),
     ((1, 32, 8, 16384, 128), True, 1),     # the long GQA workload: 8 rounds, 256 key tiles
-    ((1, 32, 8, 16384, 128), False, 0),    # no mask: every item the same length
+    ((1, 32, 8, 16384, 128), False, 1),    # no mask: 8 rounds as well
     ((2, 16, 16, 4096, 256), True, 0),     # the D = 256 workload: 2 rounds
     ((128, 8, 8, 1024, 64), True, 0),      # many rounds, 16 key tiles
     ((4, 16, 16, 8192, 128), True, 1),     # exactly 8 rounds and 128 key tiles
     ((4, 16, 16, 4096, 128), True, 0),     # 4 rounds
+    ((16, 16, 16, 4096, 128), False, 0),   # 16 rounds, but 64 key tiles
+    ((2, 16, 16, 16384, 256), False, 0),   # D = 256
     ((2, 16, 16, 16384, 256), True, 0),    # 8 rounds, but D = 256: a stolen item's K/V stream costs more
     ((4, 16, 16, 16384, 64), True, 1),     # D = 64: 11 rounds, 256 key tiles
 ]

@@ -56,33 +56,37 @@ def _inputs(B, Hq, Hkv, N, D, dtype, seed):
     return tuple(t.to(DEV) for t in workloads.make_random(B, Hq, Hkv, N, N, D, dtype, seed=seed))
 
 
-# (B, Hq, Hkv, N, D, dtype): launches that take the claimed tail (causal, D <= 128, >= 128 key tiles,
-# >= 8 rounds)
+# (B, Hq, Hkv, N, D, dtype): launches that take the claimed tail (D <= 128, >= 128 key tiles, >= 8
+# rounds; either mask)
 TAKES_TAIL = [(4, 16, 16, 8192, 128, torch.bfloat16), (1, 32, 8, 16384, 128, torch.bfloat16),
               (4, 16, 16, 16384, 64, torch.float16), (5, 16, 2, 8192, 128, torch.float16),
               (8, 16, 16, 8192, 32, torch.bfloat16)]
 
 
-@pytest.mark.parametrize("shape", TAKES_TAIL, ids=[f"b{s[0]}h{s[1]}kv{s[2]}n{s[3]}d{s[4]}" for s in TAKES_TAIL])
-def test_balanced_is_bitwise_fa_fwd_and_leaves_counters_zero(shape):
+CASES = [(s, True) for s in TAKES_TAIL] + [(TAKES_TAIL[1], False), (TAKES_TAIL[2], False)]
+
+
+@pytest.mark.parametrize("shape,causal", CASES,
+                         ids=[f"b{s[0]}h{s[1]}kv{s[2]}n{s[3]}d{s[4]}-{'c' if c else 'n'}" for s, c in CASES])
+def test_balanced_is_bitwise_fa_fwd_and_leaves_counters_zero(shape, causal):
     B, Hq, Hkv, N, D, dtype = shape
-    print(f"[case] balanced {shape}", flush=True)
-    assert _binding.fa_fwd_balance_applies(B, Hq, Hkv, N, N, D, True, dtype)
+    print(f"[case] balanced {shape} causal={causal}", flush=True)
+    assert _binding.fa_fwd_balance_applies(B, Hq, Hkv, N, N, D, causal, dtype)
     q, k, v = _inputs(B, Hq, Hkv, N, D, dtype, seed=4000 + N // 64 + D)
     stream = torch.cuda.current_stream(DEV)
     counters = torch.zeros(_binding.BALANCE_COUNTERS, dtype=torch.int32, device=DEV)
-    o_ref, l_ref = _static(q, k, v, True, stream)
+    o_ref, l_ref = _static(q, k, v, causal, stream)
     for rep in range(3):  # call after call on one buffer
-        o, lse = _balanced(q, k, v, True, counters, stream)
+        o, lse = _balanced(q, k, v, causal, counters, stream)
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"call {rep}: outputs differ from fa_fwd"
         assert not counters.any(), f"call {rep}: counters left {counters.tolist()}"
 
 
 @pytest.mark.parametrize("shape,causal", [((4, 16, 16, 1024, 128), True), ((4, 16, 16, 1024, 128), False),
-                                          ((4, 16, 16, 4096, 128), True), ((1, 32, 8, 16384, 128), False),
+                                          ((4, 16, 16, 4096, 128), True), ((16, 16, 16, 4096, 128), False),
                                           ((2, 16, 16, 16384, 256), True)],
-                         ids=["bench-causal", "bench-full", "n4096-causal", "gqa-full", "d256-causal"])
+                         ids=["bench-causal", "bench-full", "n4096-causal", "n4096-full", "d256-causal"])
 def test_static_launches_leave_counters_untouched(shape, causal):
     B, Hq, Hkv, N, D = shape
     assert not _binding.fa_fwd_balance_applies(B, Hq, Hkv, N, N, D, causal, torch.bfloat16)
