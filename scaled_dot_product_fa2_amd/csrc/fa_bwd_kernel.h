@@ -33,6 +33,8 @@
 //    in the forward), then dQ^T += K^T dS^T with transposing reads of the K tile.
 #pragma once
 
+#include <type_traits>
+
 #include "fa_fwd_kernel.h"
 
 namespace fa {
@@ -648,6 +650,11 @@ __global__ void __launch_bounds__(Cfg::THREADS)
           if (MASKED) pv = (koff > limit || koff < lower) ? 0.f : pv;
           st[kb][r] = pv * (dpt[kb][r] - dlt);  // dS^T / scale
         }
+      // (fp16) dS as opaque fp32 registers, from which both of its dtype terms below are converted
+      if constexpr (std::is_same<T, _Float16>::value) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) __asm__("" : "+v"(st[kb]));
+      }
     };
     if (WINDOW || kpos + BKV > nkv || (CAUSAL && kpos + BKV - 1 > wq0))
       probs(IC<1>());
@@ -656,8 +663,12 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     // dS enters the dQ product as two terms of the input dtype, hi = round(dS) and lo = round(dS - hi),
     // so the product sees dS to about twice the dtype's precision: where dQ is a sum of terms that
     // cancel (keys sharing a large component), one rounding of dS would dominate the result.
-    // The remainder is taken from dS as stored (no multiply-add contraction with the product that
-    // formed it), so every instance, masked or not, rounds the same values.
+    // Both terms must come from one fp32 value. The backend can fold a conversion to fp16 into the
+    // multiply that formed dS (a mixed-precision multiply-add: one rounding of the exact product)
+    // for one use of hi and not for another, so that the operand hi and the hi the remainder is
+    // taken from differ by one unit in the last place where the product lies next to a rounding
+    // midpoint; the empty asm at the end of probs() makes dS opaque fp32 registers, from which every
+    // use converts. (bf16 has no such fused conversion: its conversions take fp32 operands.)
     auto ds_terms = [&](int ks, vec8& hi_v, vec8& lo_v) {
 #pragma clang fp contract(off)
 #pragma unroll

@@ -20,8 +20,12 @@ Delta -- each element's error is, to first order in the dtype's unit roundoff u 
 rounding toward zero inside the matrix units), at most the sum of:
 
   (1) rounding the rounded factor of each term: u * sum|terms| (P for dV, dS for dK); the two-term
-      dS of dQ leaves u^2 * sum|terms|. In fp16 a value can round into the subnormal range, whose
-      spacing is 2^-24: add 2^-25 per visible term times the other factor's magnitude;
+      dS of dQ leaves u^2 * sum|terms|. Near zero the errors are absolute instead: rounding to
+      the dtype can land in its subnormal range (spacing 2^-24 in fp16, 2^-133 in bf16), an error
+      of eta = half that spacing; and an fp32 intermediate below f = 2^-126 (a probability of a
+      score far below the row maximum, the dS it forms) may be flushed to zero by the hardware.
+      Per visible term: (eta + f) times the other factor's magnitude, plus f |dP_ij - Delta_i|
+      times it for dK and dQ, where a flushed probability drops P (dP - Delta);
   (2) Delta formed from the stored O: d_i = Delta16_i - Delta_i moves dS_ij by -P_ij d_i, giving
       scale sum_i P_ij |d_i| |Q_id| for dK and scale |d_i| sum_j P_ij |K_jd| for dQ;
   (3) the recomputed probabilities: relative error at most e_ij = |lse16_i - lse_i| + scale D w
@@ -31,8 +35,8 @@ rounding toward zero inside the matrix units), at most the sum of:
   (4) dP~ and Delta16 in fp32: D w (sum_d |dO_id v_jd| + sum_d |O16_id dO_id|) on (dP - Delta),
       times P_ij and the other factor, for dK and dQ;
   (5) the fp32 accumulation of the n terms of each gradient sum: n w * sum|terms|;
-  (6) the final rounding of the gradient to the dtype: u (|exact| + the above), plus half the
-      subnormal spacing in fp16 (2^-25: a tiny gradient can round into that range or to zero).
+  (6) the final rounding of the gradient to the dtype: u (|exact| + the above), plus eta + f of
+      (1) (a tiny gradient can round into the subnormal range, be flushed or round to zero).
 
 Terms of second order (products of two of these relative errors) are neglected; the comparison
 uses no empirical factor. A kernel bug (a wrong term, mask, index or scale) makes errors of the
@@ -49,7 +53,8 @@ from oracle.attention_bwd import softmax_rows
 
 W32 = 2.0 ** -23  # fp32 rounding per operation, doubled: covers rounding toward zero in the matrix units
 UNIT = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
-SUBNORMAL_HALF = {torch.bfloat16: 0.0, torch.float16: 2.0 ** -25}
+SUBNORMAL_HALF = {torch.bfloat16: 2.0 ** -134, torch.float16: 2.0 ** -25}  # eta: half the dtype's subnormal spacing
+FP32_FLUSH = 2.0 ** -126  # f: fp32's smallest normal, below which an intermediate may be flushed to zero
 
 
 def _f64(x) -> np.ndarray:
@@ -66,7 +71,7 @@ def head_bwd_bound(qh, kh, vh, doh, o16h, lse16h, *, causal: bool, scale: float,
     qh, kh, vh: the 16-bit inputs (any float array); doh: dO; o16h, lse16h: the forward's stored
     O and LSE of this head (all rows)."""
     q, k, v, do, o16, lse16 = (_f64(t) for t in (qh, kh, vh, doh, o16h, lse16h))
-    u, eta = UNIT[dtype], SUBNORMAL_HALF[dtype]
+    u, eta, f = UNIT[dtype], SUBNORMAL_HALF[dtype], FP32_FLUSH
     n_q, D = q.shape
     n_kv = k.shape[0]
     r = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -85,37 +90,38 @@ def head_bwd_bound(qh, kh, vh, doh, o16h, lse16h, *, causal: bool, scale: float,
     ds16_abs = np.abs(p * (dp - delta16[:, None]))                        # |dS| / scale as the kernel forms it
     g = D * W32 * (np.abs(do[r]) @ np.abs(v).T + np.sum(np.abs(o16[r] * do[r]), axis=1)[:, None])   # (4)
     k_abs, q_abs, do_abs = np.abs(k), np.abs(q[r]), np.abs(do[r])
+    near0 = vis * ((eta + f) + f * np.abs(dp - delta16[:, None]))        # (1) near zero, dK and dQ
     # dQ_i = scale sum_j dS_ij K_j, two terms per key
     bq = scale * ((u * u + 2 * n_kv * W32) * (ds16_abs @ k_abs)          # (1), (5)
-                  + eta * (vis @ k_abs)                                    # (1) fp16 subnormals
+                  + near0 @ k_abs                                          # (1) near zero
                   + np.abs(d)[:, None] * (p @ k_abs)                       # (2)
                   + (ds16_abs * e) @ k_abs                                 # (3)
                   + (p * g) @ k_abs)                                       # (4)
-    bq = _stored(bq, scale * ((p * (dp - delta[:, None])) @ k), u, eta)  # (6)
+    bq = _stored(bq, scale * ((p * (dp - delta[:, None])) @ k), u, eta + f)  # (6)
     if dq_only:
         return bq, None, None
     # dK_j = scale sum_i dS_ij Q_i; the group's heads and the rows of all tiles are n_q terms here
     bk = scale * ((u + n_q * W32) * (ds16_abs.T @ q_abs)
-                  + eta * (vis.T @ q_abs)
+                  + near0.T @ q_abs
                   + (p * np.abs(d)[:, None]).T @ q_abs
                   + (ds16_abs * e).T @ q_abs
                   + (p * g).T @ q_abs)
     # dV_j = sum_i P_ij dO_i
-    bv = (u + n_q * W32) * (p.T @ do_abs) + eta * (vis.T @ do_abs) + (p * e).T @ do_abs
+    bv = (u + n_q * W32) * (p.T @ do_abs) + (eta + f) * (vis.T @ do_abs) + (p * e).T @ do_abs
     # (6) is applied once to the whole sum over query heads and rows: see finish_kv
     return bq, bk, bv
 
 
-def _stored(b_rest, exact, u, eta):
+def _stored(b_rest, exact, u, floor):
     """(6): the stored value is the computed one rounded, which is within b_rest of the exact one:
-    |rnd(x) - exact| <= b_rest + u (|exact| + b_rest) + half the subnormal spacing (fp16)."""
-    return b_rest * (1 + u) + u * np.abs(exact) + eta
+    |rnd(x) - exact| <= b_rest + u (|exact| + b_rest) + floor (eta + f: the absolute error near zero)."""
+    return b_rest * (1 + u) + u * np.abs(exact) + floor
 
 
 def finish_kv(bk_rest, bv_rest, dk_exact, dv_exact, dtype):
     """Add (6) to the summed dK and dV bounds of a key/value head (its query heads' parts added)."""
-    u, eta = UNIT[dtype], SUBNORMAL_HALF[dtype]
-    return _stored(bk_rest, dk_exact, u, eta), _stored(bv_rest, dv_exact, u, eta)
+    u, floor = UNIT[dtype], SUBNORMAL_HALF[dtype] + FP32_FLUSH
+    return _stored(bk_rest, dk_exact, u, floor), _stored(bv_rest, dv_exact, u, floor)
 
 
 def _row_lse(q, k, r, causal, scale, window):

@@ -117,6 +117,28 @@ def test_random_backward(c):
     assert_within_bound((dq, dk, dv), refs, bounds, f"backward {_id(c)}")
 
 
+# Drawn cases kept because they once failed:
+#  * an fp16 window case whose dQ missed its bound by 5 % where the two dtype terms of one large dS
+#    were converted from different roundings of it (one dS next to an fp16 rounding midpoint;
+#    tests/test_isa.py checks the generated code for the cause);
+#  * a bf16 causal case with Nkv > Nq and peaked rows, where the exact dK and dV of the last row's
+#    diagonal key are about 1e-42 and the kernel stores 0 (below bf16's smallest subnormal), and a
+#    bf16 D = 256 window case with five query rows whose exact dK of one key is 2.7e-37 and comes
+#    out 0 (its probabilities lie below fp32's smallest normal): the bound had no absolute floor
+#    near zero for bf16 and none for a flushed probability (tests/grad_bound.py, eta and f).
+REGRESSION = [dict(D=32, dtype=torch.float16, B=1, Hkv=2, Hq=8, Nq=105, Nkv=181, mask="window", left=84, right=47,
+                   q_layout="bsnd", kv_layout="bsnd", scale=0.27857336768124596, q_mult=4.0, seed=7002062),
+              dict(D=128, dtype=torch.bfloat16, B=2, Hkv=2, Hq=2, Nq=572, Nkv=1168, mask="causal", left=61, right=179,
+                   q_layout="bsnd", kv_layout="bsnd", scale=0.3699197098836212, q_mult=4.0, seed=8002222),
+              dict(D=256, dtype=torch.bfloat16, B=1, Hkv=1, Hq=1, Nq=5, Nkv=105, mask="window", left=196, right=55,
+                   q_layout="bnsd", kv_layout="bsnd", scale=0.3631942927492421, q_mult=4.0, seed=9002454)]
+
+
+@pytest.mark.parametrize("c", REGRESSION, ids=[_id(c) for c in REGRESSION])
+def test_backward_regression(c):
+    test_random_backward(c)
+
+
 # Packed variable-length sequences: a random number of sequences with random query and key lengths
 # (empty ones included), head dim, dtype, head group and mask, through the varlen entry points.
 def _draw_varlen(n: int, seed: int):
