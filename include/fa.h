@@ -89,7 +89,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * fa_fwd_balanced - fa_fwd for callers that can lend it a small counter buffer, with which long
- * causal launches even out the uneven clocks of the chip's XCDs. The schedule of fa_fwd gives
+ * launches even out the uneven clocks of the chip's XCDs. The schedule of fa_fwd gives
  * every workgroup the same work, so a launch ends when its slowest XCD does; here, in a dense
  * launch (either mask) at D <= 128 with a key range of at least 128 tiles and at least 8 rounds of items, the last
  * rounds of each XCD's list (its shortest items) are claimed through the counters instead, and
