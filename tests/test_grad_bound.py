@@ -89,3 +89,41 @@ def test_single_term_ds_where_dq_cancels(dtype, causal):
     single, _, _ = _emulate(q, k, v, do, causal, scale, dtype, two_term=False)
     if dtype == torch.bfloat16 or causal:
         assert gb.bound_ratio(single[0], exact[0], bq) > 1.0, "a single-term dS passes the dQ bound"
+
+
+def test_floor_near_zero_covers_a_flushed_probability():
+    """bf16: a key whose probabilities lie far below fp32's normal range (score 96 below the row
+    maximum, P about 2e-42) has exact dK and dV of about 1e-43; hardware that flushes such an fp32
+    probability to zero stores 0. The bound's absolute floors near zero (eta and f) must cover that
+    and be what covers it: without them the same result is outside the bound."""
+    dtype = torch.bfloat16
+    n, d, scale = 8, 16, 0.25
+    q = np.zeros((n, d))
+    q[:, 0] = 1.0
+    k = np.zeros((n, d))
+    k[1, 0] = -384.0  # scores 96 below the others
+    rng = np.random.default_rng(3)
+    v = _rnd(rng.standard_normal((n, d)), dtype)
+    do = _rnd(rng.standard_normal((n, d)), dtype)
+    exact = oracle.head_bwd_ref(q, k, v, do, causal=False, scale=scale)
+    assert 0 < np.max(np.abs(exact[1][1])) < 1e-40 and 0 < np.max(np.abs(exact[2][1])) < 1e-40
+    o, lse = oracle.attention_ref(q[None, None], k[None, None], v[None, None], causal=False, scale=scale)
+    o16 = _rnd(o[0, 0], dtype)
+    lse16 = lse[0, 0].astype(np.float32).astype(np.float64)
+    p = oracle.attention_bwd.softmax_rows(q, k, np.arange(n), False, scale)
+    p_kernel = np.where(p < 2.0 ** -126, 0.0, p)  # flushed to zero
+    ds = p_kernel * (do @ v.T - np.sum(o16 * do, axis=1)[:, None])
+    got_dk = _rnd(scale * (_rnd(ds, dtype).T @ q), dtype)
+    got_dv = _rnd(_rnd(p_kernel, dtype).T @ do, dtype)
+    assert not got_dk[1].any() and not got_dv[1].any()
+    _, bk, bv = gb.head_bwd_bound(q, k, v, do, o16, lse16, causal=False, scale=scale, dtype=dtype)
+    bk, bv = gb.finish_kv(bk, bv, exact[1], exact[2], dtype)
+    assert gb.bound_ratio(got_dk, exact[1], bk) <= 1.0 and gb.bound_ratio(got_dv, exact[2], bv) <= 1.0
+    saved = gb.SUBNORMAL_HALF[dtype], gb.FP32_FLUSH
+    try:
+        gb.SUBNORMAL_HALF[dtype], gb.FP32_FLUSH = 0.0, 0.0
+        _, bk0, bv0 = gb.head_bwd_bound(q, k, v, do, o16, lse16, causal=False, scale=scale, dtype=dtype)
+        bk0, bv0 = gb.finish_kv(bk0, bv0, exact[1], exact[2], dtype)
+    finally:
+        gb.SUBNORMAL_HALF[dtype], gb.FP32_FLUSH = saved
+    assert gb.bound_ratio(got_dk, exact[1], bk0) > 1.0 and gb.bound_ratio(got_dv, exact[2], bv0) > 1.0
