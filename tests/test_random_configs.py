@@ -8,8 +8,15 @@ within the forward tolerances, dQ, dK and dV within the derived error bound of t
 Packed variable-length sequences are drawn the same way (sequence count, query and key lengths with
 empty sequences among them, head dim, dtype, group, mask) and go through the varlen entry points.
 The case list is fixed by the seed; each case prints its draw before it runs.
+
+Wider draws are opt-in: FA_RANDOM_SWEEP=<n> in the environment adds, per family, n forward and
+n/2 backward cases with longer sequences (up to 2 000 rows), with batches and head counts that
+give the persistent schedule several rounds, and with extreme scores (Q x 8 to x 32, scales up to
+1.5), plus n/4 forward and n/8 backward packed batches of up to 24 sequences of up to 4 000 tokens.
 """
 from __future__ import annotations
+
+import os
 
 import numpy as np
 import pytest
@@ -139,6 +146,56 @@ def test_backward_regression(c):
     test_random_backward(c)
 
 
+# Opt-in wider draws (FA_RANDOM_SWEEP=<n>): families "long", "rounds" and "scores", each seeded on its own.
+N_WIDE = int(os.environ.get("FA_RANDOM_SWEEP", "0"))
+
+
+def _draw_wide(n: int, seed: int, family: str, backward: bool):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([16, 32, 64, 128, 256]))
+        dtype = [torch.bfloat16, torch.float16][int(rng.integers(2))]
+        mask = str(rng.choice(["full", "causal", "window"]))
+        if family == "rounds":  # enough items for several rounds of the persistent grid
+            hkv = int(rng.choice([1, 2, 4, 8]))
+            B, Hq, hi = int(rng.integers(1, 9)), hkv * int(rng.choice([1, 2, 4])), 1100
+            if backward:  # keep the host-side bound affordable
+                B, g = min(B, 2), Hq // hkv
+                hkv = min(hkv, 2)
+                Hq = hkv * g
+        else:
+            hkv = int(rng.choice([1, 2, 3]))
+            B, Hq = int(rng.integers(1, 3)), hkv * int(rng.choice([1, 2, 3, 4]))
+            hi = (1200 if backward else 2000) if family == "long" and rng.random() < 0.35 else 330
+        q_mult = float(rng.choice([8.0, 16.0, 32.0])) if family == "scores" else float(rng.choice([1.0, 1.0, 4.0]))
+        if family == "scores":
+            scale = float(rng.uniform(0.3, 1.5)) if rng.random() < 0.7 else None
+        else:
+            scale = None if rng.random() < 0.5 else float(rng.uniform(0.03, 0.4))
+        cases.append(dict(D=D, dtype=dtype, B=B, Hkv=hkv, Hq=Hq, Nq=int(rng.integers(1, hi)),
+                          Nkv=int(rng.integers(1, hi)), mask=mask, left=int(rng.integers(-1, 600)),
+                          right=int(rng.integers(-1, 200)), q_layout=str(rng.choice(["bnsd", "bsnd"])),
+                          kv_layout=str(rng.choice(["bnsd", "bsnd"])), scale=scale, q_mult=q_mult,
+                          seed=seed * 1000 + i))
+    return cases
+
+
+WIDE_FWD = [c for k, fam in enumerate(("long", "rounds", "scores")) for c in _draw_wide(N_WIDE, 50 + 2 * k, fam, False)]
+WIDE_BWD = [c for k, fam in enumerate(("long", "rounds", "scores"))
+            for c in _draw_wide(N_WIDE // 2, 51 + 2 * k, fam, True)]
+
+
+if N_WIDE:  # defined only when asked for, so that the default suite collects no empty parameter sets
+    @pytest.mark.parametrize("c", WIDE_FWD, ids=[_id(c) for c in WIDE_FWD])
+    def test_wide_forward(c):
+        test_random_forward(c)
+
+    @pytest.mark.parametrize("c", WIDE_BWD, ids=[_id(c) for c in WIDE_BWD])
+    def test_wide_backward(c):
+        test_random_backward(c)
+
+
 # Packed variable-length sequences: a random number of sequences with random query and key lengths
 # (empty ones included), head dim, dtype, head group and mask, through the varlen entry points.
 def _draw_varlen(n: int, seed: int):
@@ -160,8 +217,35 @@ def _draw_varlen(n: int, seed: int):
     return cases
 
 
-VL_FWD = _draw_varlen(16, 41)
-VL_BWD = _draw_varlen(8, 43)
+def _draw_varlen_wide(n: int, seed: int, backward: bool):
+    """Up to 24 sequences of up to 4 000 tokens (backward: 8 of up to 1 200), empty ones among them."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        nseq = int(rng.integers(1, 25))
+        hi = int(rng.choice([300, 1500, 4000]))
+        lens_q = [int(x) if rng.random() > 0.1 else 0 for x in rng.integers(1, hi, nseq)]
+        lens_k = [int(x) if rng.random() > 0.1 else 0 for x in rng.integers(1, hi, nseq)]
+        if rng.random() < 0.5:
+            lens_k = list(lens_q)
+        hkv = int(rng.choice([1, 2, 4]))
+        Hq = hkv * int(rng.choice([1, 2, 4]))
+        if backward:
+            lens_q, lens_k = [min(x, 1200) for x in lens_q][:8], [min(x, 1200) for x in lens_k][:8]
+            Hq, hkv = min(Hq, 4), min(hkv, 2)
+            Hq -= Hq % hkv
+        if sum(lens_q) == 0:
+            lens_q[0] = 5
+        if sum(lens_k) == 0:
+            lens_k[-1] = 7
+        cases.append(dict(lens_q=lens_q, lens_k=lens_k, Hkv=hkv, Hq=Hq, D=int(rng.choice([16, 32, 64, 128, 256])),
+                          dtype=[torch.bfloat16, torch.float16][int(rng.integers(2))],
+                          causal=bool(rng.integers(2)), seed=seed * 1000 + i))
+    return cases
+
+
+VL_FWD = _draw_varlen(16, 41) + _draw_varlen_wide(N_WIDE // 4, 61, False)
+VL_BWD = _draw_varlen(8, 43) + _draw_varlen_wide(N_WIDE // 8, 63, True)
 
 
 def _vl_id(c):
