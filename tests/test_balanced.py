@@ -6,13 +6,16 @@ so its outputs must be bitwise those of fa_fwd on every launch, the ones that ta
 must be left zero after every call, so that a buffer can serve call after call on one stream;
 buffers of two streams must not interfere. Parity of the values themselves with the float64
 oracle is covered by the forward parity tests, which run through the same entry point (the long
-GQA workload among them takes the claimed tail).
+GQA workload among them takes the claimed tail). FA_RANDOM_SWEEP=<n> in the environment adds n/10
+seeded random long launches of 8 192-20 000 tokens, compared the same way.
 """
 from __future__ import annotations
 
 import ctypes
 import math
+import os
 
+import numpy as np
 import pytest
 import torch
 
@@ -136,6 +139,40 @@ def test_two_streams_with_their_own_buffers():
         assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
         assert torch.equal(o2, o2_ref) and torch.equal(lse2, l2_ref)
     assert not c1.any() and not c2.any()
+
+
+# Opt-in (FA_RANDOM_SWEEP=<n>): n/10 seeded random long launches, most of which take the claimed tail,
+# each bitwise against fa_fwd with the counters left zero.
+def _draw_long(n: int, seed: int):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(rng.choice([32, 64, 128]))
+        hkv = int(rng.choice([3, 4, 5, 8]))
+        Hq, B = hkv * int(rng.choice([2, 4])), int(rng.integers(2, 5))
+        N = int(rng.integers(8192, 20000))
+        Nk = N if rng.random() < 0.6 else int(rng.integers(8192, 20000))
+        out.append((B, Hq, hkv, N, Nk, D, bool(rng.integers(2)), [torch.bfloat16, torch.float16][int(rng.integers(2))],
+                    seed * 100 + i))
+    return out
+
+
+LONG = _draw_long(int(os.environ.get("FA_RANDOM_SWEEP", "0")) // 10, 71)
+if LONG:  # defined only when asked for
+    @pytest.mark.parametrize("case", LONG, ids=[f"b{c[0]}h{c[1]}kv{c[2]}-{c[3]}x{c[4]}-d{c[5]}-{'c' if c[6] else 'n'}"
+                                                for c in LONG])
+    def test_random_long_launch_is_bitwise_fa_fwd(case):
+        B, Hq, Hkv, N, Nk, D, causal, dtype, seed = case
+        print(f"[case] balanced random {case}", flush=True)
+        q, k, v = (t.to(DEV) for t in workloads.make_random(B, Hq, Hkv, N, Nk, D, dtype, seed=seed))
+        stream = torch.cuda.current_stream(DEV)
+        counters = torch.zeros(_binding.BALANCE_COUNTERS, dtype=torch.int32, device=DEV)
+        o_ref, l_ref = _static(q, k, v, causal, stream)
+        for _ in range(2):
+            o, lse = _balanced(q, k, v, causal, counters, stream)
+            torch.cuda.synchronize()
+            assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+            assert not counters.any()
 
 
 def test_binding_forward_uses_the_stream_buffer():
